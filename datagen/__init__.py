@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs shared by the oracle side and the HIP side.
+
+This module only draws numbers; it contains none of the GEMM or copy
+arithmetic. Every value is a pure function of (seed, index), so the CPU and
+the GPU sides of a test receive identical bytes.
+
+Generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014) used counter-style. The 64-bit word for
+stream ``seed`` at position ``i`` is ``mix64(GAMMA * (seed * 2**40 + i + 1))``
+where ``mix64`` is SplitMix64's output finaliser. Distributions built on it:
+
+* ``uniform_pm1``: U[-1, 1) on the 2**-23 grid, ``(top24 - 2**23) * 2**-23``,
+  exact in fp32 and fp64 and never -0.0 (values in [-1, 1 - 2**-23]).
+* ``normal01``: Box-Muller in fp64 from two 24-bit uniforms (the first mapped
+  to (0, 1]), rounded to fp32.
+* ``coarse_pm1``: the 2**-4 grid in [-1, 15/16]; with K <= 8192 every fp32
+  partial sum of products of such values is exact.
+* ``page_pattern_a/b``: the inputs of the day-74 program on the
+  "pipelined_gemm.cu" page (main: a[i] = (i % 97) * 0.01f,
+  b[i] = (i % 53) * 0.02f - 0.5f).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_CHUNK = 1 << 22
+
+SEED_A = 1
+SEED_B = 2
+SEED_COPY = 3
+
+
+def mix64(z: np.ndarray) -> np.ndarray:
+    """SplitMix64's output finaliser on a uint64 array (wrapping arithmetic)."""
+    z = z.copy()
+    z ^= z >> np.uint64(30)
+    z *= _M1
+    z ^= z >> np.uint64(27)
+    z *= _M2
+    z ^= z >> np.uint64(31)
+    return z
+
+
+def words(seed: int, start: int, count: int) -> np.ndarray:
+    """64-bit words of stream ``seed`` at positions start .. start+count-1."""
+    ctr = np.arange(start + 1, start + 1 + count, dtype=np.uint64)
+    ctr += np.uint64((seed << 40) & 0xFFFFFFFFFFFFFFFF)
+    with np.errstate(over="ignore"):
+        return mix64(ctr * GAMMA)
+
+
+def _fill(n: int, fn) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, _CHUNK):
+        c = min(_CHUNK, n - s)
+        out[s:s + c] = fn(s, c)
+    return out
+
+
+def uniform_pm1(seed: int, n: int) -> np.ndarray:
+    """n values of U[-1, 1) on the 2**-23 grid (fp32, exact)."""
+    def part(s, c):
+        top = (words(seed, s, c) >> np.uint64(40)).astype(np.int64)
+        return ((top - (1 << 23)).astype(np.float64) * 2.0 ** -23).astype(np.float32)
+    return _fill(n, part)
+
+
+def coarse_pm1(seed: int, n: int) -> np.ndarray:
+    """n values on the 2**-4 grid in [-1, 15/16] (fp32, exact)."""
+    def part(s, c):
+        top = (words(seed, s, c) >> np.uint64(59)).astype(np.int64)
+        return ((top - 16).astype(np.float64) / 16.0).astype(np.float32)
+    return _fill(n, part)
+
+
+def normal01(seed: int, n: int) -> np.ndarray:
+    """n values ~ N(0, 1): Box-Muller in fp64, rounded to fp32."""
+    def part(s, c):
+        w = words(seed, 2 * s, 2 * c)
+        u1 = ((w[0::2] >> np.uint64(40)).astype(np.float64) + 1.0) * 2.0 ** -24
+        u2 = (w[1::2] >> np.uint64(40)).astype(np.float64) * 2.0 ** -24
+        return (np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)).astype(np.float32)
+    return _fill(n, part)
+
+
+def page_pattern_a(n: int) -> np.ndarray:
+    i = np.arange(n, dtype=np.int64)
+    return (i % 97).astype(np.float32) * np.float32(0.01)
+
+
+def page_pattern_b(n: int) -> np.ndarray:
+    i = np.arange(n, dtype=np.int64)
+    return (i % 53).astype(np.float32) * np.float32(0.02) - np.float32(0.5)
+
+
+def matrix(kind: str, seed: int, rows: int, cols: int, ld: int | None = None,
+           pad: float = float("nan")) -> np.ndarray:
+    """A rows x ld fp32 array whose [:, :cols] block holds the stream's first
+    rows*cols values in row-major order; columns cols..ld-1 hold ``pad``."""
+    ld = cols if ld is None else ld
+    if ld < cols:
+        raise ValueError("ld < cols")
+    n = rows * cols
+    gen = {"uniform": uniform_pm1, "coarse": coarse_pm1, "normal": normal01}
+    if kind in gen:
+        v = gen[kind](seed, n)
+    elif kind == "ones":
+        v = np.ones(n, dtype=np.float32)
+    elif kind == "page_a":
+        v = page_pattern_a(n)
+    elif kind == "page_b":
+        v = page_pattern_b(n)
+    else:
+        raise ValueError(kind)
+    out = np.full((rows, ld), pad, dtype=np.float32)
+    out[:, :cols] = v.reshape(rows, cols)
+    return out
+
+
+def slice_sentinel(rows: int, cols: int, axis: int, group: int = 16) -> np.ndarray:
+    """Matrix whose entry is floor(index_along_axis / group); used as the B
+    operand (axis=0, index k) or the A operand (axis=1, index k)."""
+    idx = np.arange(rows if axis == 0 else cols, dtype=np.int64) // group
+    if axis == 0:
+        return np.repeat(idx[:, None], cols, axis=1).astype(np.float32)
+    return np.repeat(idx[None, :], rows, axis=0).astype(np.float32)
+
+
+# ---- torch twin (same numbers, generated on any torch device) -------------
+
+def _torch_words(seed: int, start: int, count: int, device):
+    import torch
+    def u(x):  # uint64 constant as a wrapped int64
+        return x - (1 << 64) if x >= (1 << 63) else x
+    ctr = torch.arange(start + 1, start + 1 + count, dtype=torch.int64, device=device)
+    ctr = ctr + u((seed << 40) & 0xFFFFFFFFFFFFFFFF)
+    z = ctr * u(int(GAMMA))
+
+    def lsr(x, s):  # logical shift right on int64 bit patterns
+        return (x >> s) & ((1 << (64 - s)) - 1)
+    z = z ^ lsr(z, 30)
+    z = z * u(int(_M1))
+    z = z ^ lsr(z, 27)
+    z = z * u(int(_M2))
+    z = z ^ lsr(z, 31)
+    return z, lsr
+
+
+def uniform_pm1_torch(seed: int, n: int, device="cpu"):
+    """Same values as uniform_pm1, produced by torch on ``device``."""
+    import torch
+    out = torch.empty(n, dtype=torch.float32, device=device)
+    step = 1 << 24
+    for s in range(0, n, step):
+        c = min(step, n - s)
+        z, lsr = _torch_words(seed, s, c, device)
+        top = lsr(z, 40)
+        out[s:s + c] = ((top - (1 << 23)).to(torch.float64) * 2.0 ** -23).to(torch.float32)
+    return out
+
+
+def normal01_torch(seed: int, n: int, device="cpu"):
+    """Same values as normal01, produced by torch on ``device``."""
+    import torch
+    out = torch.empty(n, dtype=torch.float32, device=device)
+    step = 1 << 23
+    for s in range(0, n, step):
+        c = min(step, n - s)
+        z, lsr = _torch_words(seed, 2 * s, 2 * c, device)
+        u1 = (lsr(z[0::2], 40).to(torch.float64) + 1.0) * 2.0 ** -24
+        u2 = lsr(z[1::2], 40).to(torch.float64) * 2.0 ** -24
+        out[s:s + c] = (torch.sqrt(-2.0 * torch.log(u1)) * torch.cos(2.0 * np.pi * u2)).to(torch.float32)
+    return out

@@ -1,0 +1,126 @@
+"""TEST INFRASTRUCTURE: the CPU oracle for the pipelined FP32 GEMM and tile copy.
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this package. The product library never loads it, and it shares no code
+with the HIP sources (see ref_gemm.c for the definitions and their sources).
+
+The numeric work happens in ``ref_gemm.c`` (plain C, fp64, OpenMP over rows);
+this module only compiles it with gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "ref_gemm.c")
+LIB = os.path.join(_HERE, "_build", "liboracle.so")
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+          "-shared", "-fPIC", "-std=c99", "-Wall"]
+
+_lib = None
+
+
+def build(src: str = SRC, out: str = LIB) -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *CFLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(LIB))
+    return _lib
+
+
+def _bind(lib):
+    i64, fp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+    for name in ("oracle_gemm_f64", "oracle_abs_gemm_f64"):
+        f = getattr(lib, name)
+        f.argtypes = [i64, i64, i64, fp, i64, fp, i64, dp, i64]
+        f.restype = None
+    lib.oracle_copy_f32.argtypes = [i64, i64, fp, i64, fp, i64]
+    lib.oracle_copy_f32.restype = None
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check_operands(M, N, K, A, B):
+    for name, x in (("A", A), ("B", B)):
+        if x.dtype != np.float32 or x.ndim != 2 or (x.size and x.strides[1] != 4):
+            raise TypeError(f"{name} must be a 2-D fp32 array with unit column stride")
+    if A.shape[0] < M or A.shape[1] < K or B.shape[0] < K or B.shape[1] < N:
+        raise ValueError("operand smaller than M x K / K x N")
+
+
+def gemm_f64(A: np.ndarray, B: np.ndarray, M=None, N=None, K=None, lib=None) -> np.ndarray:
+    """C_ref = A[:M,:K] @ B[:K,:N] in fp64 (k ascending). A and B may be
+    views with a row stride larger than their width (their leading dimension)."""
+    M = A.shape[0] if M is None else M
+    K = A.shape[1] if K is None else K
+    N = B.shape[1] if N is None else N
+    _check_operands(M, N, K, A, B)
+    C = np.empty((M, N), dtype=np.float64)
+    (lib or load()).oracle_gemm_f64(M, N, K, _ptr(A), A.strides[0] // 4,
+                                    _ptr(B), B.strides[0] // 4, _ptr(C), N)
+    return C
+
+
+def abs_gemm_f64(A: np.ndarray, B: np.ndarray, M=None, N=None, K=None, lib=None) -> np.ndarray:
+    """Abs = |A[:M,:K]| @ |B[:K,:N]| in fp64."""
+    M = A.shape[0] if M is None else M
+    K = A.shape[1] if K is None else K
+    N = B.shape[1] if N is None else N
+    _check_operands(M, N, K, A, B)
+    C = np.empty((M, N), dtype=np.float64)
+    (lib or load()).oracle_abs_gemm_f64(M, N, K, _ptr(A), A.strides[0] // 4,
+                                        _ptr(B), B.strides[0] // 4, _ptr(C), N)
+    return C
+
+
+def copy_f32(src: np.ndarray, rows=None, cols=None, lib=None) -> np.ndarray:
+    rows = src.shape[0] if rows is None else rows
+    cols = src.shape[1] if cols is None else cols
+    dst = np.full((rows, cols), np.nan, dtype=np.float32)  # unwritten cells stay NaN
+    (lib or load()).oracle_copy_f32(rows, cols, _ptr(src), src.strides[0] // 4, _ptr(dst), cols)
+    return dst
+
+
+def bound(K: int, Abs: np.ndarray, slack: float = 4.0) -> np.ndarray:
+    """Elementwise acceptance bound slack * K * 2^-24 * (|A||B|)_ij for an fp32
+    GEMM against this fp64 reference."""
+    return slack * K * 2.0 ** -24 * Abs
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).oracle_num_threads())
+
+
+def timed_gemm_rows(A: np.ndarray, B: np.ndarray, rows: int, lib=None):
+    """Run oracle_gemm_f64 on the first ``rows`` rows of A (full N and K) and
+    return (seconds, flop). Used only for the CPU baseline."""
+    M, K = rows, A.shape[1]
+    N = B.shape[1]
+    C = np.empty((M, N), dtype=np.float64)
+    lib = lib or load()
+    t0 = time.perf_counter()
+    lib.oracle_gemm_f64(M, N, K, _ptr(A), A.strides[0] // 4, _ptr(B), B.strides[0] // 4, _ptr(C), N)
+    dt = time.perf_counter() - t0
+    return dt, 2.0 * M * N * K
