@@ -1,0 +1,179 @@
+"""Python binding of libmgemm: the MI355X (gfx950) pipelined FP32 GEMM and tile copy.
+
+The functions named ``mgemm_*`` are the C entry points of ``include/mgemm.h``
+with the same arguments (device pointers as integers, ``stream`` as the
+integer value of a hipStream_t). ``sgemm`` and ``tile_copy`` are conveniences
+that read pointers, leading dimensions and the current stream off torch
+tensors. Every step of the computation runs in the HIP kernels of
+``csrc/``; this module only marshals arguments. If the compiled library is
+missing, importing the functions raises instead of computing anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libmgemm.so")
+ISA_PATH = os.path.join(_HERE, "_build", "mgemm-gfx950.s")
+
+# constants of include/mgemm.h
+MGEMM_VERSION = 100
+FILL_SYNC, FILL_PIPED = 0, 1
+COMPUTE_VALU, COMPUTE_MFMA = 0, 1
+TILE_AUTO, TILE_64x64, TILE_128x128 = 0, 1, 2
+LOADER_AUTO, LOADER_B128, LOADER_B32 = 0, 1, 2
+OK, ERR_ARG, ERR_ALIAS, ERR_ARCH, ERR_LAUNCH, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+
+_FILL = {"sync": FILL_SYNC, "piped": FILL_PIPED}
+_COMPUTE = {"valu": COMPUTE_VALU, "mfma": COMPUTE_MFMA}
+_TILE = {"auto": TILE_AUTO, "64x64": TILE_64x64, "128x128": TILE_128x128}
+_LOADER = {"auto": LOADER_AUTO, "b128": LOADER_B128, "b32": LOADER_B32}
+
+
+class MgemmError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {mgemm_status_string(status)} (status {status})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "compute", "tile", "bm", "bn", "bk", "threads", "blocks", "load_bytes", "slices",
+        "stages", "fill_mode", "lds_bytes", "loads_per_slice", "max_vmcnt")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmgemm (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libmgemm is not built ({LIB_PATH} missing); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.mgemm_sgemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, vp]
+        L.mgemm_sgemm_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci, vp]
+        L.mgemm_tile_copy.argtypes = [i64, i64, vp, i64, vp, i64, ci, vp]
+        L.mgemm_plan_sgemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci,
+                                       ctypes.POINTER(Plan)]
+        L.mgemm_ring_trace.argtypes = [ci, ci, ci, ci, ctypes.POINTER(ctypes.c_int), ci]
+        L.mgemm_status_string.argtypes = [ci]
+        L.mgemm_status_string.restype = ctypes.c_char_p
+        for f in (L.mgemm_sgemm, L.mgemm_sgemm_ex, L.mgemm_tile_copy, L.mgemm_plan_sgemm,
+                  L.mgemm_ring_trace, L.mgemm_version):
+            f.restype = ci
+        _lib = L
+    return _lib
+
+
+# ---- the C entry points, same names and arguments ---------------------------
+
+def mgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, stream) -> int:
+    return lib().mgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, stream)
+
+
+def mgemm_sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader, stream) -> int:
+    return lib().mgemm_sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader, stream)
+
+
+def mgemm_tile_copy(rows, cols, src, lds, dst, ldd, stages, stream) -> int:
+    return lib().mgemm_tile_copy(rows, cols, src, lds, dst, ldd, stages, stream)
+
+
+def mgemm_status_string(status: int) -> str:
+    return lib().mgemm_status_string(status).decode()
+
+
+def mgemm_version() -> int:
+    return lib().mgemm_version()
+
+
+def mgemm_plan_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader):
+    """(status, Plan) for these arguments; no device access."""
+    p = Plan()
+    st = lib().mgemm_plan_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader,
+                                ctypes.byref(p))
+    return st, p
+
+
+def mgemm_ring_trace(kind: int, stages: int, fill_mode: int, slices: int):
+    """The ring schedule as a list of (op, a, b) events (see include/mgemm.h)."""
+    n = lib().mgemm_ring_trace(kind, stages, fill_mode, slices, None, 0)
+    if n < 0:
+        raise MgemmError(n, "mgemm_ring_trace")
+    buf = (ctypes.c_int * (3 * max(n, 1)))()
+    lib().mgemm_ring_trace(kind, stages, fill_mode, slices, buf, n)
+    return [(buf[3 * i], buf[3 * i + 1], buf[3 * i + 2]) for i in range(n)]
+
+
+# ---- torch conveniences (pointers, leading dimensions and stream only) ------
+
+def _mat(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D float32 torch tensor")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be on a GPU")
+    if t.numel() and t.stride(1) != 1:
+        raise TypeError(f"{name} must have unit column stride")
+    return t.data_ptr(), max(t.stride(0), t.shape[1])
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+def sgemm(A, B, C=None, *, stages: int = 2, fill: str = "piped", compute: str = "valu",
+          tile: str = "auto", loader: str = "auto", stream=None):
+    """C = A @ B through mgemm_sgemm_ex on the current (or given) stream."""
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C has the wrong shape")
+    pa, lda = _mat(A, "A")
+    pb, ldb = _mat(B, "B")
+    pc, ldc = _mat(C, "C")
+    st = mgemm_sgemm_ex(M, N, K, pa, lda, pb, ldb, pc, ldc, stages, _FILL[fill], _COMPUTE[compute],
+                        _TILE[tile], _LOADER[loader], _stream(stream))
+    if st != OK:
+        raise MgemmError(st, "mgemm_sgemm_ex")
+    return C
+
+
+def tile_copy(src, dst=None, *, stages: int = 3, stream=None):
+    """dst = src through mgemm_tile_copy."""
+    import torch
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=torch.float32, device=src.device)
+    if tuple(dst.shape) != tuple(src.shape):
+        raise ValueError("dst has the wrong shape")
+    ps, lds = _mat(src, "src")
+    pd, ldd = _mat(dst, "dst")
+    st = mgemm_tile_copy(src.shape[0], src.shape[1], ps, lds, pd, ldd, stages, _stream(stream))
+    if st != OK:
+        raise MgemmError(st, "mgemm_tile_copy")
+    return dst
+
+
+def plan(M, N, K, *, stages=2, fill="piped", compute="valu", tile="auto", loader="auto",
+         a_ptr=0x10000, lda=None, b_ptr=0x40000000, ldb=None, c_ptr=0x80000000, ldc=None):
+    """Launch plan for a problem (defaults: aligned, non-overlapping fake addresses)."""
+    st, p = mgemm_plan_sgemm(M, N, K, a_ptr, K if lda is None else lda, b_ptr, N if ldb is None else ldb,
+                             c_ptr, N if ldc is None else ldc, stages, _FILL[fill], _COMPUTE[compute],
+                             _TILE[tile], _LOADER[loader])
+    if st != OK:
+        raise MgemmError(st, "mgemm_plan_sgemm")
+    return p.as_dict()

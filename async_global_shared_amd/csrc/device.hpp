@@ -1,0 +1,579 @@
+// device.hpp -- gfx950 kernels of the pipelined FP32 GEMM and the tile copy.
+//
+// Structure (what each part restates from the pages):
+//  * Layout / Operand: one K slice of A (BM x BK) or B (BK x BN) in LDS as
+//    16-byte chunks. The pages' kernels move one float4 per thread per operand
+//    per slice at the same addresses in both fills ("Day 74 -- Async copies
+//    and pipelines", section "Two kernels, one arithmetic"); here each lane
+//    owns a fixed list of chunks (4-byte pieces when alignment forbids 16-byte
+//    loads) and both fills deliver exactly the same bytes to exactly the same
+//    LDS positions.
+//  * The asynchronous fill is gfx950's buffer_load ... lds: the wave issues it
+//    and continues; the data goes from memory into LDS without a VGPR (the
+//    role cp.async plays on the pages). Its LDS destination is M0 + lane*size,
+//    so a wave instruction writes one contiguous run; bank-conflict-free reads
+//    come from choosing which global chunk each lane fetches (an XOR swizzle
+//    of the chunk index per row).
+//  * Out-of-range elements are loaded through a buffer offset beyond the
+//    descriptor's range, which reads zero, so ragged tiles hold +0.0 and never
+//    stale data ("cp.async" TVM page, section "Predication is different from
+//    zero fill").
+//  * ValuTile / MfmaTile: the one computeTile both fills call
+//    ("pipelined_gemm.cu", computeTile): VALU is an explicit fma chain per C
+//    element with k ascending; MFMA uses v_mfma_f32_32x32x2_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "ring.h"
+
+namespace mgemm {
+
+typedef __attribute__((address_space(3))) void lds_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kBK = 16;
+// Every buffer descriptor spans 2^31 bytes from its (per-block, per-slice)
+// base; valid lanes use offsets below that, masked lanes use kMasked, which the
+// range check turns into a zero read with no memory access.
+constexpr unsigned kRecords = 0x80000000u;
+constexpr unsigned kMasked = 0x80000000u;
+constexpr int kDescWord3 = 0x00020000; // raw buffer, 32-bit data format
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)kRecords, kDescWord3);
+}
+
+// ---- LDS layouts ----------------------------------------------------------
+
+struct SwzNone {
+    MG_HD static constexpr int f(int) { return 0; }
+};
+// VALU A tiles: the 4 thread rows of a wave read rows 4 apart.
+struct SwzValuA {
+    MG_HD static constexpr int f(int r) { return (r >> 2) & 3; }
+};
+// MFMA A tiles: 32 lanes read 32 consecutive rows; distinct banks for any 8
+// (32-bank view) or 16 (64-bank view) consecutive rows.
+struct SwzMfmaA {
+    MG_HD static constexpr int f(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+};
+// MFMA B tiles: lane halves read rows k and k+4; put them 128 B apart.
+struct SwzMfmaB {
+    MG_HD static constexpr int f(int r) { return ((r >> 2) & 1) << 3; }
+};
+
+// ROWS x COLS fp32 slice; chunk (r, c4) (4 floats) lives at chunk position
+// r * CPR + (c4 ^ f(r)).
+template <int ROWS, int COLS, class Swz>
+struct Layout {
+    static constexpr int kRows = ROWS, kCols = COLS;
+    static constexpr int CPR = COLS / 4;
+    static constexpr int CHUNKS = ROWS * CPR;
+    static constexpr int BYTES = CHUNKS * 16;
+    static_assert(COLS % 4 == 0 && CHUNKS % (64 * kWaves) == 0, "whole wave instructions per slice");
+    MG_HD static constexpr int pos(int r, int c4) { return r * CPR + (c4 ^ Swz::f(r)); }
+    MG_HD static constexpr int row(int p) { return p / CPR; }
+    MG_HD static constexpr int col4(int p) { return (p % CPR) ^ Swz::f(p / CPR); }
+};
+
+// ---- one operand's slice loader --------------------------------------------
+//
+// Unit i of wave w covers wave-instruction g = i*WAVES + w. With 16-byte
+// loads lane l owns chunk position p = g*64 + l; with 4-byte loads it owns
+// float q = g*64 + l of the slice (chunk q/4, element q%4). The LDS byte
+// address is g*64*W + l*W in both cases, for the asynchronous and the
+// register fill alike.
+template <class L, int W, int WAVES = kWaves>
+struct Operand {
+    static constexpr int U = (W == 16) ? L::CHUNKS / (64 * WAVES) : (L::CHUNKS * 4) / (64 * WAVES);
+    static_assert(W == 16 || W == 4, "load width");
+    int rr[U], cc[U], off[U];
+
+    __device__ void init(int lane, int wave, int ld) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int g = i * WAVES + wave;
+            int r, c;
+            if constexpr (W == 16) {
+                const int p = g * 64 + lane;
+                r = L::row(p);
+                c = 4 * L::col4(p);
+            } else {
+                const int q = g * 64 + lane;
+                r = L::row(q >> 2);
+                c = 4 * L::col4(q >> 2) + (q & 3);
+            }
+            rr[i] = r;
+            cc[i] = c;
+            off[i] = r * ld + c;
+        }
+    }
+    // byte offset within the operand's region of a slot, for unit i of wave w
+    __device__ static constexpr int lds_off(int i, int wave) { return (i * WAVES + wave) * 64 * W; }
+
+    __device__ unsigned voff(int i, int rowlim, int collim) const {
+        return (rr[i] < rowlim && cc[i] < collim) ? (unsigned)off[i] * 4u : kMasked;
+    }
+};
+
+// ---- compute tiles ----------------------------------------------------------
+
+// VALU: 256 threads as 16 x 16; thread (tr, tc) owns rows 64h + 4tr + i and
+// columns 64hn + 4tc + j (h < TM/4, hn < TN/4, i, j < 4).
+template <int BM, int BN, int TM, int TN, class SA>
+struct ValuTile {
+    using LA = Layout<BM, kBK, SA>;
+    using LB = Layout<kBK, BN, SwzNone>;
+    static constexpr int HM = TM / 4, HN = TN / 4;
+    static_assert(BM == 64 * HM && BN == 64 * HN, "16 x 16 threads, 4-row groups 64 apart");
+    float acc[TM][TN];
+    int tr, tc;
+
+    __device__ void init(int tid) {
+        tr = tid >> 4;
+        tc = tid & 15;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = 0.0f;
+    }
+    __device__ int row(int h, int i) const { return 64 * h + 4 * tr + i; }
+    __device__ int col(int h) const { return 64 * h + 4 * tc; }
+
+    // acc[i][j] = fma(A[row_i][k], B[k][col_j], acc[i][j]) for k = 0 .. BK-1
+    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
+#pragma unroll
+        for (int kc = 0; kc < kBK / 4; ++kc) {
+            f32x4 a[TM];
+#pragma unroll
+            for (int h = 0; h < HM; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a[4 * h + i] = *(const f32x4 *)(As + LA::pos(row(h, i), kc) * 16);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                f32x4 b[HN];
+#pragma unroll
+                for (int h = 0; h < HN; ++h)
+                    b[h] = *(const f32x4 *)(Bs + LB::pos(4 * kc + kk, col(h) >> 2) * 16);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int h = 0; h < HN; ++h)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][4 * h + j] = __builtin_fmaf(a[i][kk], b[h][j], acc[i][4 * h + j]);
+            }
+        }
+    }
+
+    __device__ void store(float *C, int ldc, int m0, int n0, int M, int N, bool vec) const {
+#pragma unroll
+        for (int h = 0; h < HM; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = m0 + row(h, i);
+                if (r >= M)
+                    continue;
+#pragma unroll
+                for (int hn = 0; hn < HN; ++hn) {
+                    const int c = n0 + col(hn);
+                    float *p = C + (size_t)r * ldc + c;
+                    const float *v = &acc[4 * h + i][4 * hn];
+                    if (vec && c + 3 < N) {
+                        *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (c + j < N)
+                                p[j] = v[j];
+                    }
+                }
+            }
+    }
+};
+
+// MFMA: 4 waves as 2 x 2; each wave owns WTM x WTN tiles of 32 x 32, computed
+// with v_mfma_f32_32x32x2_f32. Lane l supplies A[m0 + l%32][k_l] and
+// B[k_l][n0 + l%32] with k_l = 8kb + 4(l/32) + s in MFMA step s, so the four
+// steps of a half slice cover its eight k values.
+template <int WTM, int WTN>
+struct MfmaTile {
+    static constexpr int BM = 64 * WTM, BN = 64 * WTN;
+    using LA = Layout<BM, kBK, SwzMfmaA>;
+    using LB = Layout<kBK, BN, SwzMfmaB>;
+    f32x16 acc[WTM][WTN];
+    int wm, wn, lane;
+
+    __device__ void init(int tid) {
+        lane = tid & 63;
+        const int w = tid >> 6;
+        wm = w >> 1;
+        wn = w & 1;
+#pragma unroll
+        for (int a = 0; a < WTM; ++a)
+#pragma unroll
+            for (int b = 0; b < WTN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[a][b][i] = 0.0f;
+    }
+
+    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
+        const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int kb = 0; kb < kBK / 8; ++kb) {
+            f32x4 a[WTM];
+#pragma unroll
+            for (int ta = 0; ta < WTM; ++ta) {
+                const int m = 32 * WTM * wm + 32 * ta + l32;
+                a[ta] = *(const f32x4 *)(As + LA::pos(m, 2 * kb + h) * 16);
+            }
+            float b[WTN][4];
+#pragma unroll
+            for (int tb = 0; tb < WTN; ++tb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int k = 8 * kb + 4 * h + s;
+                    const int n = 32 * WTN * wn + 32 * tb + l32;
+                    b[tb][s] = *(const float *)(Bs + LB::pos(k, n >> 2) * 16 + (n & 3) * 4);
+                }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int ta = 0; ta < WTM; ++ta)
+#pragma unroll
+                    for (int tb = 0; tb < WTN; ++tb)
+                        acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ta][s], b[tb][s], acc[ta][tb], 0, 0, 0);
+        }
+    }
+
+    __device__ void store(float *C, int ldc, int m0, int n0, int M, int N, bool) const {
+        const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int ta = 0; ta < WTM; ++ta)
+#pragma unroll
+            for (int tb = 0; tb < WTN; ++tb) {
+                const int c = n0 + 32 * WTN * wn + 32 * tb + l32;
+                if (c >= N)
+                    continue;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = m0 + 32 * WTM * wm + 32 * ta + (i >> 2) * 8 + h * 4 + (i & 3);
+                    if (r < M)
+                        C[(size_t)r * ldc + c] = acc[ta][tb][i];
+                }
+            }
+    }
+};
+
+// Tile configurations (block tile, compute tile).
+struct CfgValu64 {
+    using Tile = ValuTile<64, 64, 4, 4, SwzValuA>;
+    static constexpr int BM = 64, BN = 64;
+};
+struct CfgValu128 {
+    using Tile = ValuTile<128, 128, 8, 8, SwzValuA>;
+    static constexpr int BM = 128, BN = 128;
+};
+struct CfgMfma64 {
+    using Tile = MfmaTile<1, 1>;
+    static constexpr int BM = 64, BN = 64;
+};
+struct CfgMfma128 {
+    using Tile = MfmaTile<2, 2>;
+    static constexpr int BM = 128, BN = 128;
+};
+
+// ---- block -> C tile ----------------------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b on XCD
+// b % 8), each with its own L2. Give each XCD a contiguous range of logical
+// tiles, then walk the logical order 8 tile-rows down before moving right, so
+// the blocks resident on one XCD share A and B panels in its L2.
+__device__ inline void block_tile(int bid, int gm, int gn, int &tm, int &tn) {
+    const int nb = gm * gn;
+    const int x = bid & 7, i = bid >> 3;
+    const int q = nb >> 3, r = nb & 7;
+    const int lin = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+    constexpr int G = 8;
+    const int per_group = G * gn;
+    const int grp = lin / per_group;
+    const int first = grp * G;
+    const int rows = min(G, gm - first);
+    const int in = lin - grp * per_group;
+    tm = first + in % rows;
+    tn = in / rows;
+}
+
+// ---- waits and barriers --------------------------------------------------------
+
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Block barrier after this wave's LDS reads and writes have completed.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int M, N, K;
+    int lda, ldb, ldc;
+    int gm, gn;
+    int vec_store;
+};
+
+template <int W>
+struct RegOf {
+    using type = u32x4;
+};
+template <>
+struct RegOf<4> {
+    using type = unsigned;
+};
+
+// State one block of the GEMM shares between its ring operations.
+template <class Tile, int W>
+struct GemmCtx {
+    using LA = typename Tile::LA;
+    using LB = typename Tile::LB;
+    using OA = Operand<LA, W>;
+    using OB = Operand<LB, W>;
+    static constexpr int SLOT = LA::BYTES + LB::BYTES;
+
+    OA oa;
+    OB ob;
+    Tile tile;
+    unsigned char *smem;
+    int wave, lane;
+    const float *Ablk; // A + m0 * lda
+    const float *Bblk; // B + n0
+    int ldb, K, a_rows, b_cols;
+
+    // slice s covers A[m0.., 16s..] and B[16s.., n0..]; limits are relative
+    __device__ const float *a_ptr(int s) const { return Ablk + s * kBK; }
+    __device__ const float *b_ptr(int s) const { return Bblk + (size_t)s * kBK * ldb; }
+    __device__ int klim(int s) const { return K - s * kBK; }
+    __device__ void barrier() { lds_barrier(); }
+    __device__ void compute(int, int slot) {
+        const unsigned char *base = smem + slot * SLOT;
+        tile.compute(base, base + LA::BYTES);
+    }
+};
+
+// Asynchronous fill: buffer_load ... lds straight into the ring slot.
+template <class Tile, int W>
+struct PipedOps : GemmCtx<Tile, W> {
+    using C = GemmCtx<Tile, W>;
+    __device__ void issue(int s, int slot) {
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
+        const int k = this->klim(s);
+        unsigned char *base = this->smem + slot * C::SLOT;
+#pragma unroll
+        for (int i = 0; i < C::OA::U; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t *)(base + C::OA::lds_off(i, this->wave)), W,
+                                                      this->oa.voff(i, this->a_rows, k), 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < C::OB::U; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_t *)(base + C::LA::BYTES + C::OB::lds_off(i, this->wave)), W,
+                this->ob.voff(i, k, this->b_cols), 0, 0, 0);
+    }
+    // each slice is OA::U + OB::U fill instructions of this wave
+    template <int P>
+    __device__ void wait() {
+        wait_vm<P *(C::OA::U + C::OB::U)>();
+    }
+};
+
+// Synchronous fill: global -> register set -> LDS.
+template <class Tile, int W, int NSET>
+struct SyncOps : GemmCtx<Tile, W> {
+    using C = GemmCtx<Tile, W>;
+    using R = typename RegOf<W>::type;
+    R va[NSET][C::OA::U];
+    R vb[NSET][C::OB::U];
+
+    __device__ static R ld(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        if constexpr (W == 16)
+            return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        else
+            return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+    template <int SET>
+    __device__ void load(int s) {
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
+        const int k = this->klim(s);
+#pragma unroll
+        for (int i = 0; i < C::OA::U; ++i)
+            va[SET][i] = ld(ra, this->oa.voff(i, this->a_rows, k));
+#pragma unroll
+        for (int i = 0; i < C::OB::U; ++i)
+            vb[SET][i] = ld(rb, this->ob.voff(i, k, this->b_cols));
+    }
+    template <int SET>
+    __device__ void store(int slot) {
+        unsigned char *base = this->smem + slot * C::SLOT;
+#pragma unroll
+        for (int i = 0; i < C::OA::U; ++i)
+            *(R *)(base + C::OA::lds_off(i, this->wave) + this->lane * W) = va[SET][i];
+#pragma unroll
+        for (int i = 0; i < C::OB::U; ++i)
+            *(R *)(base + C::LA::BYTES + C::OB::lds_off(i, this->wave) + this->lane * W) = vb[SET][i];
+    }
+};
+
+template <class Cfg, int S, bool PIPED, int W>
+__global__ void __launch_bounds__(kThreads) sgemm_kernel(GemmArgs g) {
+    using Tile = typename Cfg::Tile;
+    using Ctx = GemmCtx<Tile, W>;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S * Ctx::SLOT];
+
+    int tm, tn;
+    block_tile(blockIdx.x, g.gm, g.gn, tm, tn);
+    const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+    const int tid = threadIdx.x;
+    const int T = (g.K + kBK - 1) / kBK;
+
+    using Ops = typename std::conditional<PIPED, PipedOps<Tile, W>, SyncOps<Tile, W, (S > 1 ? S - 1 : 1)>>::type;
+    Ops ops;
+    ops.smem = smem;
+    ops.lane = tid & 63;
+    ops.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    ops.Ablk = g.A + (size_t)m0 * g.lda;
+    ops.Bblk = g.B + n0;
+    ops.ldb = g.ldb;
+    ops.K = g.K;
+    ops.a_rows = g.M - m0;
+    ops.b_cols = g.N - n0;
+    ops.oa.init(ops.lane, ops.wave, g.lda);
+    ops.ob.init(ops.lane, ops.wave, g.ldb);
+    ops.tile.init(tid);
+    if constexpr (PIPED)
+        piped_schedule<S>(T, ops);
+    else
+        sync_schedule<S>(T, ops);
+    ops.tile.store(g.C, g.ldc, m0, n0, g.M, g.N, g.vec_store != 0);
+}
+
+// C[0:M, 0:N] = +0 (the empty sum, K == 0).
+__global__ void __launch_bounds__(kThreads) zero_kernel(float *C, int M, int N, int ldc) {
+    const int64_t n = (int64_t)M * N;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+        C[(i / N) * (int64_t)ldc + (i % N)] = 0.0f;
+}
+
+// ---- pipelined tile copy -----------------------------------------------------------
+//
+// dst = src through an S-slot ring of 64 x 64 fp32 LDS tiles. Waves 0-1 only
+// fill (asynchronous global -> LDS), waves 2-3 only drain (LDS -> VGPR ->
+// global). Keeping stores out of the filling waves keeps their vmcnt a pure
+// count of their own fills, so the ring's waits are exact. Block b copies
+// tiles b, b + G, b + 2G, ... (G = grid size).
+struct CopyArgs {
+    const float *src;
+    float *dst;
+    int rows, cols, lds, ldd;
+    int tcols;  // tiles per tile-row
+    int ntiles;
+};
+
+using CopyLayout = Layout<64, 64, SwzNone>;
+
+template <int W, bool VST>
+struct CopyOps {
+    static constexpr int SLOT = CopyLayout::BYTES;
+    static constexpr int PW = 2; // filling waves
+    using OP = Operand<CopyLayout, W, PW>;
+    CopyArgs a;
+    OP op;
+    unsigned char *smem;
+    int wave, lane, G;
+    bool producer;
+
+    __device__ void coords(int t, int &r0, int &c0) const {
+        const int id = (int)blockIdx.x + t * G;
+        r0 = (id / a.tcols) * 64;
+        c0 = (id % a.tcols) * 64;
+    }
+    __device__ void issue(int t, int slot) {
+        if (!producer)
+            return;
+        int r0, c0;
+        coords(t, r0, c0);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.src + (size_t)r0 * a.lds + c0);
+        unsigned char *base = smem + slot * SLOT;
+#pragma unroll
+        for (int i = 0; i < OP::U; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t *)(base + OP::lds_off(i, wave)), W,
+                                                      op.voff(i, a.rows - r0, a.cols - c0), 0, 0, 0);
+    }
+    template <int P>
+    __device__ void wait() {
+        if (producer)
+            wait_vm<P * OP::U>();
+    }
+    __device__ void barrier() { lds_barrier(); }
+    __device__ void compute(int t, int slot) {
+        if (producer)
+            return;
+        int r0, c0;
+        coords(t, r0, c0);
+        const unsigned char *base = smem + slot * SLOT;
+        const int cw = wave - PW; // drains chunk rows 32cw .. 32cw+31
+        constexpr int PER = CopyLayout::CHUNKS / (64 * PW);
+        f32x4 v[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            v[j] = *(const f32x4 *)(base + ((cw * PER + j) * 64 + lane) * 16);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int p = (cw * PER + j) * 64 + lane;
+            const int r = r0 + CopyLayout::row(p);
+            const int c = c0 + 4 * CopyLayout::col4(p);
+            if (r >= a.rows)
+                continue;
+            float *d = a.dst + (size_t)r * a.ldd + c;
+            if constexpr (VST) {
+                if (c < a.cols)
+                    __builtin_nontemporal_store(v[j], (f32x4 *)d);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c + e < a.cols)
+                        d[e] = v[j][e];
+            }
+        }
+    }
+};
+
+template <int S, int W, bool VST>
+__global__ void __launch_bounds__(kThreads) tile_copy_kernel(CopyArgs a) {
+    using Ops = CopyOps<W, VST>;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S * Ops::SLOT];
+    Ops ops;
+    ops.a = a;
+    ops.smem = smem;
+    ops.lane = threadIdx.x & 63;
+    ops.wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    ops.producer = ops.wave < Ops::PW;
+    ops.G = gridDim.x;
+    ops.op.init(ops.lane, ops.producer ? ops.wave : 0, a.lds);
+    const int T = (a.ntiles - (int)blockIdx.x + ops.G - 1) / ops.G;
+    piped_schedule<S>(T, ops);
+}
+
+} // namespace mgemm

@@ -1,0 +1,343 @@
+// mgemm.hip -- the C ABI (include/mgemm.h): argument validation, the launch
+// plan, the gfx950 gate and kernel dispatch for the pipelined FP32 GEMM and
+// tile copy of device.hpp.
+//
+// The pages' program refuses a device without the asynchronous copy before
+// allocating anything ("pipelined_gemm.cu", main: capability gate) and
+// rejects shapes and stage counts its kernels cannot run at compile time
+// (static_asserts beside the tile constants). A library cannot exit, so the
+// same refusals become status codes returned before any work is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "device.hpp"
+#include "mgemm.h"
+
+using namespace mgemm;
+
+namespace {
+
+constexpr int64_t kMaxLd = int64_t(1) << 22;     // keeps every in-block byte offset below 2^31
+constexpr int64_t kMaxExtent = int64_t(1) << 31; // rows * ld per operand, in elements
+constexpr int64_t kAutoBigTileBlocks = 512;      // 128x128 tiles once they give >= 2 blocks per CU
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [lo, hi) byte range of a rows x cols row-major block with leading dimension ld
+struct Range {
+    uintptr_t lo = 0, hi = 0;
+};
+Range span(const void *p, int64_t rows, int64_t cols, int64_t ld) {
+    Range r;
+    if (rows > 0 && cols > 0) {
+        r.lo = reinterpret_cast<uintptr_t>(p);
+        r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + cols) * 4);
+    }
+    return r;
+}
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+int check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld) {
+    if (rows < 0 || cols < 0 || ld < 0)
+        return MGEMM_ERR_ARG;
+    if (rows > 0 && cols > 0) {
+        if (p == nullptr || ld < cols)
+            return MGEMM_ERR_ARG;
+        if (ld >= kMaxLd || rows * ld >= kMaxExtent)
+            return MGEMM_ERR_UNSUPPORTED;
+    }
+    return MGEMM_OK;
+}
+
+int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+              const float *C, int64_t ldc, int stages, int fill, int compute, int tile, int loader,
+              mgemm_plan_t *pl) {
+    if (M < 0 || N < 0 || K < 0)
+        return MGEMM_ERR_ARG;
+    if (stages < 1 || stages > 3 || (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED) ||
+        (compute != MGEMM_COMPUTE_VALU && compute != MGEMM_COMPUTE_MFMA) || tile < MGEMM_TILE_AUTO ||
+        tile > MGEMM_TILE_128x128 || loader < MGEMM_LOADER_AUTO || loader > MGEMM_LOADER_B32)
+        return MGEMM_ERR_ARG;
+    int st;
+    if ((st = check_matrix(A, M, K, lda)) != MGEMM_OK || (st = check_matrix(B, K, N, ldb)) != MGEMM_OK ||
+        (st = check_matrix(C, M, N, ldc)) != MGEMM_OK)
+        return st;
+    if (M >= kMaxExtent || N >= kMaxExtent || K >= kMaxExtent)
+        return MGEMM_ERR_UNSUPPORTED;
+    const Range rc = span(C, M, N, ldc);
+    if (overlap(rc, span(A, M, K, lda)) || overlap(rc, span(B, K, N, ldb)))
+        return MGEMM_ERR_ALIAS;
+
+    // 16-byte lanes need every chunk wholly inside or outside its operand:
+    // aligned bases, ld multiple of 4 and contiguous extent multiple of 4.
+    const bool b128_ok = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0 && K % 4 == 0 && N % 4 == 0;
+    int W;
+    if (loader == MGEMM_LOADER_B128) {
+        if (!b128_ok)
+            return MGEMM_ERR_ARG;
+        W = 16;
+    } else if (loader == MGEMM_LOADER_B32) {
+        W = 4;
+    } else {
+        W = b128_ok ? 16 : 4;
+    }
+
+    if (tile == MGEMM_TILE_AUTO) {
+        const int64_t nb128 = ((M + 127) / 128) * ((N + 127) / 128);
+        tile = nb128 >= kAutoBigTileBlocks ? MGEMM_TILE_128x128 : MGEMM_TILE_64x64;
+    }
+    const int b = tile == MGEMM_TILE_128x128 ? 128 : 64;
+    mgemm_plan_t p;
+    std::memset(&p, 0, sizeof p);
+    p.compute = compute;
+    p.tile = tile;
+    p.bm = b;
+    p.bn = b;
+    p.bk = kBK;
+    p.threads = kThreads;
+    p.blocks = (int)(((M + b - 1) / b) * ((N + b - 1) / b));
+    p.load_bytes = W;
+    p.slices = (int)((K + kBK - 1) / kBK);
+    p.stages = stages;
+    p.fill_mode = fill;
+    p.lds_bytes = stages * (b * kBK + kBK * b) * 4;
+    // one 64-lane instruction moves 64*W bytes; a slice of both operands is
+    // 2*b*16*4 bytes, shared by the 4 waves
+    p.loads_per_slice = (2 * b * kBK * 4) / (64 * W) / kWaves;
+    p.max_vmcnt = fill == MGEMM_FILL_PIPED ? (stages >= 3 ? (stages - 2) * p.loads_per_slice : 0) : 0;
+    if (pl)
+        *pl = p;
+    return MGEMM_OK;
+}
+
+// ---- device gate --------------------------------------------------------------
+
+std::atomic<int> g_arch[64]; // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[64];
+
+int current_device(int *dev) {
+    if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= 64)
+        return MGEMM_ERR_ARCH;
+    int a = g_arch[*dev].load(std::memory_order_relaxed);
+    if (a == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, *dev) != hipSuccess)
+            return MGEMM_ERR_ARCH;
+        a = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_cus[*dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        g_arch[*dev].store(a, std::memory_order_relaxed);
+    }
+    return a == 1 ? MGEMM_OK : MGEMM_ERR_ARCH;
+}
+
+// ---- kernel tables ----------------------------------------------------------------
+
+template <class Cfg, int S, int W>
+constexpr const void *gk(bool piped) {
+    return piped ? (const void *)&sgemm_kernel<Cfg, S, true, W> : (const void *)&sgemm_kernel<Cfg, S, false, W>;
+}
+template <class Cfg>
+const void *gemm_kernel(int S, bool piped, int W) {
+    if (W == 16) {
+        switch (S) {
+        case 1: return gk<Cfg, 1, 16>(piped);
+        case 2: return gk<Cfg, 2, 16>(piped);
+        default: return gk<Cfg, 3, 16>(piped);
+        }
+    }
+    switch (S) {
+    case 1: return gk<Cfg, 1, 4>(piped);
+    case 2: return gk<Cfg, 2, 4>(piped);
+    default: return gk<Cfg, 3, 4>(piped);
+    }
+}
+
+template <int S>
+const void *ck(int W, bool vst) {
+    if (W == 16)
+        return vst ? (const void *)&tile_copy_kernel<S, 16, true> : (const void *)&tile_copy_kernel<S, 16, false>;
+    return vst ? (const void *)&tile_copy_kernel<S, 4, true> : (const void *)&tile_copy_kernel<S, 4, false>;
+}
+const void *copy_kernel(int S, int W, bool vst) {
+    switch (S) {
+    case 1: return ck<1>(W, vst);
+    case 2: return ck<2>(W, vst);
+    default: return ck<3>(W, vst);
+    }
+}
+
+int launch(const void *fn, int blocks, void *arg, hipStream_t stream) {
+    void *args[] = {arg};
+    const hipError_t e = hipLaunchKernel(fn, dim3(blocks), dim3(kThreads), args, 0, stream);
+    return e == hipSuccess ? MGEMM_OK : MGEMM_ERR_LAUNCH;
+}
+
+// ---- host recorder for mgemm_ring_trace ----------------------------------------------
+
+struct Recorder {
+    int *ev;
+    int cap, n;
+    void put(int op, int a, int b) {
+        if (n < cap) {
+            ev[3 * n] = op;
+            ev[3 * n + 1] = a;
+            ev[3 * n + 2] = b;
+        }
+        ++n;
+    }
+    void issue(int s, int slot) { put(1, s, slot); }
+    template <int P>
+    void wait() { put(2, P, 0); }
+    void barrier() { put(3, 0, 0); }
+    void compute(int s, int slot) { put(4, s, slot); }
+    template <int SET>
+    void store(int slot) { put(5, SET, slot); }
+    template <int SET>
+    void load(int s) { put(6, s, SET); }
+};
+
+} // namespace
+
+extern "C" {
+
+const char *mgemm_status_string(int s) {
+    switch (s) {
+    case MGEMM_OK: return "ok";
+    case MGEMM_ERR_ARG: return "invalid argument";
+    case MGEMM_ERR_ALIAS: return "output overlaps an input";
+    case MGEMM_ERR_ARCH: return "current device is not gfx950 (or no device)";
+    case MGEMM_ERR_LAUNCH: return "kernel launch failed";
+    case MGEMM_ERR_UNSUPPORTED: return "extent beyond the supported addressing range";
+    default: return "unknown status";
+    }
+}
+
+int mgemm_version(void) { return MGEMM_VERSION; }
+
+int mgemm_plan_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+                     const float *C, int64_t ldc, int stages, int fill_mode, int compute, int tile, int loader,
+                     mgemm_plan_t *plan) {
+    return plan_gemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader, plan);
+}
+
+int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+                   float *C, int64_t ldc, int stages, int fill_mode, int compute, int tile, int loader,
+                   void *stream) {
+    mgemm_plan_t p;
+    int st = plan_gemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader, &p);
+    if (st != MGEMM_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return MGEMM_OK;
+    int dev;
+    if ((st = current_device(&dev)) != MGEMM_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (K == 0) {
+        const int64_t n = M * N;
+        const int blocks = (int)std::min<int64_t>((n + kThreads - 1) / kThreads, 4096);
+        int m = (int)M, nn = (int)N, l = (int)ldc;
+        void *args[] = {&C, &m, &nn, &l};
+        const hipError_t e = hipLaunchKernel((const void *)&zero_kernel, dim3(blocks), dim3(kThreads), args, 0, s);
+        return e == hipSuccess ? MGEMM_OK : MGEMM_ERR_LAUNCH;
+    }
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.lda = (int)lda;
+    g.ldb = (int)ldb;
+    g.ldc = (int)ldc;
+    g.gm = (int)((M + p.bm - 1) / p.bm);
+    g.gn = (int)((N + p.bn - 1) / p.bn);
+    g.vec_store = aligned16(C) && ldc % 4 == 0;
+    const bool piped = fill_mode == MGEMM_FILL_PIPED;
+    const void *fn;
+    if (compute == MGEMM_COMPUTE_VALU)
+        fn = p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgValu128>(stages, piped, p.load_bytes)
+                                          : gemm_kernel<CfgValu64>(stages, piped, p.load_bytes);
+    else
+        fn = p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgMfma128>(stages, piped, p.load_bytes)
+                                          : gemm_kernel<CfgMfma64>(stages, piped, p.load_bytes);
+    return launch(fn, p.blocks, &g, s);
+}
+
+int mgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+                float *C, int64_t ldc, int stages, int fill_mode, void *stream) {
+    return mgemm_sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, MGEMM_COMPUTE_VALU, MGEMM_TILE_AUTO,
+                          MGEMM_LOADER_AUTO, stream);
+}
+
+int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, float *dst, int64_t ldd, int stages,
+                    void *stream) {
+    if (stages < 1 || stages > 3)
+        return MGEMM_ERR_ARG;
+    int st;
+    if ((st = check_matrix(src, rows, cols, lds)) != MGEMM_OK || (st = check_matrix(dst, rows, cols, ldd)) != MGEMM_OK)
+        return st;
+    if (overlap(span(src, rows, cols, lds), span(dst, rows, cols, ldd)))
+        return MGEMM_ERR_ALIAS;
+    if (rows == 0 || cols == 0)
+        return MGEMM_OK;
+    int dev;
+    if ((st = current_device(&dev)) != MGEMM_OK)
+        return st;
+    const int W = (aligned16(src) && lds % 4 == 0 && cols % 4 == 0) ? 16 : 4;
+    const bool vst = aligned16(dst) && ldd % 4 == 0 && cols % 4 == 0;
+    CopyArgs a;
+    a.src = src;
+    a.dst = dst;
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.lds = (int)lds;
+    a.ldd = (int)ldd;
+    a.tcols = (int)((cols + 63) / 64);
+    const int64_t ntiles = ((rows + 63) / 64) * a.tcols;
+    if (ntiles >= kMaxExtent)
+        return MGEMM_ERR_UNSUPPORTED;
+    a.ntiles = (int)ntiles;
+    const void *fn = copy_kernel(stages, W, vst);
+    // persistent grid: as many blocks as fit on the device at once
+    static std::atomic<int> occ_cache[3][2][2];
+    std::atomic<int> &oc = occ_cache[stages - 1][W == 16][vst];
+    int occ = oc.load(std::memory_order_relaxed);
+    if (occ == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kThreads, 0) != hipSuccess || occ < 1)
+            occ = 1;
+        oc.store(occ, std::memory_order_relaxed);
+    }
+    const int64_t resident = (int64_t)occ * g_cus[dev].load(std::memory_order_relaxed);
+    const int blocks = (int)std::min<int64_t>(ntiles, resident > 0 ? resident : 256);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch(fn, blocks, &a, s);
+}
+
+int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *events, int cap) {
+    if (stages < 1 || stages > 3 || slices < 0 || cap < 0 || (cap > 0 && events == nullptr) ||
+        (kind != 0 && kind != 1) || (fill_mode != MGEMM_FILL_SYNC && fill_mode != MGEMM_FILL_PIPED) ||
+        (kind == 1 && fill_mode != MGEMM_FILL_PIPED))
+        return MGEMM_ERR_ARG;
+    Recorder r{events, cap, 0};
+    if (fill_mode == MGEMM_FILL_PIPED) {
+        switch (stages) {
+        case 1: piped_schedule<1>(slices, r); break;
+        case 2: piped_schedule<2>(slices, r); break;
+        default: piped_schedule<3>(slices, r); break;
+        }
+    } else {
+        switch (stages) {
+        case 1: sync_schedule<1>(slices, r); break;
+        case 2: sync_schedule<2>(slices, r); break;
+        default: sync_schedule<3>(slices, r); break;
+        }
+    }
+    return r.n;
+}
+
+} // extern "C"

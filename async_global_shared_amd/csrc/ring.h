@@ -1,0 +1,124 @@
+// ring.h -- stage schedules of the LDS ring, shared by the kernels and the
+// host-side trace (mgemm_ring_trace), so the schedule that is tested on the
+// CPU is the one the GPU executes.
+//
+// The pages' pipelined kernel ("pipelined_gemm.cu", matmulTilePiped) keeps a
+// fetch counter at most kStages slices ahead of the compute counter; each
+// iteration tops up the fetches, waits for the oldest stage, computes on it
+// and releases it ("Day 74 -- Async copies and pipelines", section "Two
+// kernels, one arithmetic"). The pipeline object is a FIFO of stages whose
+// consumer_wait waits on the oldest stage only ("A study on CUDA async
+// memcpy", section "cuda::pipeline").
+//
+// On gfx950 there is no pipeline object. Completion of a wave's own
+// asynchronous global->LDS loads is counted by its vmcnt (in order), and the
+// block-wide "stage ready" and "stage released" events are one s_barrier: a
+// barrier orders threads but does not complete copies ("Day 74", section
+// "Pitfalls"), so every wave waits on its own count first, then barriers.
+#pragma once
+
+#if defined(__HIPCC__)
+#define MG_HD __host__ __device__
+#else
+#define MG_HD
+#endif
+
+namespace mgemm {
+
+template <int I>
+struct Int {
+    static constexpr int value = I;
+};
+
+template <int B, int E, class F>
+MG_HD inline void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(Int<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Asynchronous ring, `S` LDS slots. Ops provides:
+//   issue(slice, slot)   start the global->LDS fill of `slice` into `slot`
+//   wait<P>()            this wave: at most P of its issued slices in flight
+//   barrier()            block barrier after the wave's LDS reads completed
+//   compute(slice, slot) consume `slot`, which holds `slice`
+// S == 1 has no lookahead (fetch, wait, compute, release). For S >= 2 the
+// prologue issues S-1 slices; iteration t waits for slice t, barriers (slice
+// t visible to all waves; slot (t-1) % S released by all waves), refills that
+// released slot with slice t+S-1, then computes slice t.
+template <int S, class Ops>
+MG_HD inline void piped_schedule(int T, Ops &ops) {
+    static_assert(S >= 1 && S <= 3, "stages must be 1, 2 or 3");
+    if constexpr (S == 1) {
+        for (int t = 0; t < T; ++t) {
+            ops.issue(t, 0);
+            ops.template wait<0>();
+            ops.barrier();
+            ops.compute(t, 0);
+            ops.barrier();
+        }
+    } else {
+        for (int s = 0; s < S - 1 && s < T; ++s)
+            ops.issue(s, s);
+        for (int t = 0; t < T; ++t) {
+            if (t + S - 2 < T)
+                ops.template wait<S - 2>();
+            else
+                ops.template wait<0>();
+            ops.barrier();
+            if (t + S - 1 < T)
+                ops.issue(t + S - 1, (t + S - 1) % S);
+            ops.compute(t, t % S);
+        }
+    }
+}
+
+// Synchronous ring: global -> registers -> LDS. Ops provides:
+//   load<SET>(slice)      issue global->register loads of `slice` into set SET
+//   store<SET>(slot)      write register set SET to LDS `slot` (waits on loads)
+//   barrier(), compute(slice, slot) as above
+// S == 1 is the pages' matmulTileSync: load, store, barrier, compute, barrier.
+// For S >= 2 (a double buffer built from synchronous loads, as in the
+// "async copy pipeline" article's benchmark), S-1 register sets keep S-1
+// slices in flight: iteration t issues slice t+S-1, computes slice t, then
+// stores slice t+1 into its slot and barriers. Register-set indices are
+// compile-time constants (the loop is unrolled by S-1).
+template <int S, class Ops>
+MG_HD inline void sync_schedule(int T, Ops &ops) {
+    static_assert(S >= 1 && S <= 3, "stages must be 1, 2 or 3");
+    if constexpr (S == 1) {
+        for (int t = 0; t < T; ++t) {
+            ops.template load<0>(t);
+            ops.template store<0>(0);
+            ops.barrier();
+            ops.compute(t, 0);
+            ops.barrier();
+        }
+    } else {
+        constexpr int R = S - 1;
+        static_for<0, R>([&](auto s) {
+            if (s.value < T)
+                ops.template load<s.value>(s.value);
+        });
+        if (T > 0) {
+            ops.template store<0>(0);
+            ops.barrier();
+        }
+        for (int t0 = 0; t0 < T; t0 += R) {
+            static_for<0, R>([&](auto u) {
+                const int t = t0 + u.value;
+                if (t < T) {
+                    if (t + R < T)
+                        ops.template load<u.value>(t + R);
+                    ops.compute(t, t % S);
+                    if (t + 1 < T)
+                        ops.template store<(u.value + 1) % R>((t + 1) % S);
+                    ops.barrier();
+                }
+            });
+        }
+    }
+}
+
+} // namespace mgemm

@@ -1,0 +1,157 @@
+/*
+ * mgemm.h -- C ABI of the MI355X (gfx950) pipelined FP32 GEMM and tile copy.
+ *
+ * What the library computes is defined on these pages:
+ *  - "Day 74 -- Async copies and pipelines" (sections "A copy that skips the
+ *    registers", "Two kernels, one arithmetic", "Exercise"): a register-tiled
+ *    FP32 GEMM whose shared-memory tiles are filled either synchronously
+ *    (global -> register -> shared, then a barrier) or asynchronously through
+ *    a multi-stage pipeline, so that the fetch of the next K slice overlaps the
+ *    compute on the current one; both fills feed one shared computeTile and
+ *    must give bit-identical results.
+ *  - "pipelined_gemm.cu" (kernels matmulTileSync and matmulTilePiped, and
+ *    matmulCpu): the tile shapes, the per-thread float4 fill, the lookahead
+ *    loop that keeps up to kStages fetches in flight, and the reference.
+ *  - "A study on CUDA async memcpy" (section "async-group based approach"):
+ *    waiting "until at most N of the most recent groups are in flight", which
+ *    this library realises per wave with s_waitcnt vmcnt(N) and per block with
+ *    s_barrier.
+ *  - "cp.async" (TVM TIRx, section "Predication is different from zero fill"):
+ *    out-of-range parts of a tile are filled with zeros, never left unwritten.
+ *
+ * Conventions for every entry point:
+ *  - Matrices are row-major fp32 in device memory; ld* is the row stride in
+ *    elements. A is M x K (lda >= K), B is K x N (ldb >= N), C is M x N
+ *    (ldc >= N). The caller owns all buffers; the library never allocates,
+ *    never frees and never synchronises the host.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued asynchronously on it; a returned MGEMM_OK means "launched".
+ *  - Arguments are validated before any HIP call; a non-OK status means
+ *    nothing was enqueued. No entry point exits the process.
+ *  - C must not overlap A or B (the pages' kernels take __restrict__ inputs).
+ *  - Each operand extent (rows x ld) must stay below 2^31 elements and every
+ *    ld below 2^22; larger problems return MGEMM_ERR_UNSUPPORTED.
+ */
+#ifndef MGEMM_H
+#define MGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MGEMM_VERSION 100 /* 1.0.0 */
+
+/* fill_mode: how LDS tiles are filled ("Two kernels, one arithmetic"). */
+#define MGEMM_FILL_SYNC 0  /* global -> VGPR -> LDS; stages>=2 stage slices in registers */
+#define MGEMM_FILL_PIPED 1 /* asynchronous global -> LDS (buffer_load ... lds) ring */
+
+/* compute: the inner product on the LDS tiles. */
+#define MGEMM_COMPUTE_VALU 0 /* per element fma chain, k ascending (the pages' computeTile) */
+#define MGEMM_COMPUTE_MFMA 1 /* v_mfma_f32_32x32x2_f32 wave tiles */
+
+/* tile: block tile of C (BM x BN, K slice 16, 256 threads). */
+#define MGEMM_TILE_AUTO 0
+#define MGEMM_TILE_64x64 1   /* VALU: 4x4 micro-tile per thread (the pages' shape) */
+#define MGEMM_TILE_128x128 2 /* VALU: 8x8 micro-tile; MFMA: 2x2 32x32 tiles per wave */
+
+/* loader: width of each lane's global load (results never depend on it). */
+#define MGEMM_LOADER_AUTO 0 /* 16 B when bases, ld and extents allow, else 4 B */
+#define MGEMM_LOADER_B128 1 /* 16 B; refused (MGEMM_ERR_ARG) when alignment forbids it */
+#define MGEMM_LOADER_B32 2  /* 4 B, any alignment */
+
+/* status codes */
+#define MGEMM_OK 0
+#define MGEMM_ERR_ARG (-1)         /* negative size, ld too small, NULL with nonzero extent, bad enum */
+#define MGEMM_ERR_ALIAS (-2)       /* C overlaps A or B (or dst overlaps src) */
+#define MGEMM_ERR_ARCH (-3)        /* current device is not gfx950, or no device */
+#define MGEMM_ERR_LAUNCH (-4)      /* the kernel launch failed; hipGetLastError has the cause */
+#define MGEMM_ERR_UNSUPPORTED (-5) /* extent beyond the 32-bit buffer addressing limits above */
+
+/*
+ * C[0:M, 0:N] = A[0:M, 0:K] * B[0:K, 0:N]  (fp32, "Two kernels, one arithmetic").
+ * stages in {1, 2, 3}: LDS ring depth; piped keeps stages-1 slices in flight
+ * during compute (stages == 1: fetch, wait, compute, no overlap). fill_mode is
+ * MGEMM_FILL_SYNC or MGEMM_FILL_PIPED. Uses the VALU compute tile and the
+ * automatic tile and loader choice. For a fixed (shape, compute, tile), every
+ * (stages, fill_mode, loader) gives bit-identical C. M == 0 or N == 0: no-op.
+ * K == 0: C[0:M, 0:N] = +0. Cells of C outside M x N are never written.
+ */
+int mgemm_sgemm(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc,
+                int stages, int fill_mode, void *stream);
+
+/* As mgemm_sgemm with the compute variant, block tile and loader width chosen
+ * by the caller (MGEMM_COMPUTE_*, MGEMM_TILE_*, MGEMM_LOADER_*). */
+int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K,
+                   const float *A, int64_t lda,
+                   const float *B, int64_t ldb,
+                   float *C, int64_t ldc,
+                   int stages, int fill_mode, int compute, int tile, int loader,
+                   void *stream);
+
+/*
+ * dst[0:rows, 0:cols] = src[0:rows, 0:cols], streamed global -> LDS -> global
+ * in 64 x 64 tiles through a `stages`-slot LDS ring filled asynchronously
+ * (stages in {1, 2, 3}; 1 = no overlap). The bytes of dst equal those of src;
+ * padding columns of dst are not written. Isolates the fill bandwidth of the
+ * GEMM's loader ("cp.async", section "Example: four 16-byte copies per
+ * thread", which copies global -> shared -> global and checks equality).
+ */
+int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds,
+                    float *dst, int64_t ldd, int stages, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *mgemm_status_string(int status);
+
+/* MGEMM_VERSION of the loaded library. */
+int mgemm_version(void);
+
+/*
+ * The launch the library would make for these arguments, without touching
+ * the device (no HIP call). Returns the status mgemm_sgemm_ex would return
+ * from validation; on MGEMM_OK fills *plan.
+ */
+typedef struct mgemm_plan {
+    int compute;       /* MGEMM_COMPUTE_* */
+    int tile;          /* MGEMM_TILE_64x64 or MGEMM_TILE_128x128 */
+    int bm, bn, bk;    /* block tile and K slice */
+    int threads;       /* per block */
+    int blocks;        /* 1-D grid */
+    int load_bytes;    /* 16 or 4: per-lane width of each global load */
+    int slices;        /* ceil(K / bk) */
+    int stages;
+    int fill_mode;
+    int lds_bytes;     /* LDS per block: stages * (bm*bk + bk*bn) * 4 */
+    int loads_per_slice; /* vector-memory instructions per wave per K slice */
+    int max_vmcnt;     /* largest s_waitcnt vmcnt immediate the schedule uses */
+} mgemm_plan_t;
+
+int mgemm_plan_sgemm(int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     const float *C, int64_t ldc,
+                     int stages, int fill_mode, int compute, int tile, int loader,
+                     mgemm_plan_t *plan);
+
+/*
+ * Record the stage schedule that a kernel's ring executes for `slices` K
+ * slices (fill_mode, stages as above; kind 0 = GEMM, 1 = tile copy), as
+ * produced by the very template the kernels instantiate. Each event is 3 ints
+ * {op, a, b} written to events[0 .. 3*cap): op 1 = issue(slice a -> slot b),
+ * 2 = wait(at most a slices of this wave in flight), 3 = barrier,
+ * 4 = compute(slice a from slot b), 5 = store register set a -> slot b
+ * (sync fill), 6 = load slice a into register set b (sync fill).
+ * Returns the number of events (which may exceed cap; only cap are written),
+ * or MGEMM_ERR_ARG. Host only; no device needed.
+ */
+int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *events, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGEMM_H */

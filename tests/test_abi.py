@@ -1,0 +1,317 @@
+"""Host-side tests of libmgemm: exports, argument validation, launch plans,
+the ring schedule the kernels execute, and evidence in the generated gfx950
+ISA. No GPU is touched: every call here returns before any HIP call."""
+import os
+import re
+
+import pytest
+
+import async_global_shared_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mgemm.h")
+
+A0, B0, C0 = 0x100000, 0x40000000, 0x80000000  # fake, aligned, disjoint device addresses
+
+
+def test_exports_every_declared_symbol():
+    src = open(HEADER).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(mgemm_[a-z_]+)\s*\(", src, re.M))
+    assert {"mgemm_sgemm", "mgemm_sgemm_ex", "mgemm_tile_copy", "mgemm_status_string", "mgemm_version",
+            "mgemm_plan_sgemm", "mgemm_ring_trace"} <= names
+    L = m.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert m.mgemm_version() == m.MGEMM_VERSION
+    for s in (m.OK, m.ERR_ARG, m.ERR_ALIAS, m.ERR_ARCH, m.ERR_LAUNCH, m.ERR_UNSUPPORTED):
+        assert m.mgemm_status_string(s) not in ("", "unknown status")
+    assert m.mgemm_status_string(12345) == "unknown status"
+
+
+def sg(M=64, N=64, K=64, A=A0, lda=None, B=B0, ldb=None, C=C0, ldc=None, stages=2, fill=1, compute=0, tile=0,
+       loader=0):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return m.mgemm_sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stages, fill, compute, tile, loader, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(M=-1), m.ERR_ARG), (dict(N=-1), m.ERR_ARG), (dict(K=-1), m.ERR_ARG),
+    (dict(stages=0), m.ERR_ARG), (dict(stages=4), m.ERR_ARG), (dict(fill=2), m.ERR_ARG),
+    (dict(compute=2), m.ERR_ARG), (dict(tile=3), m.ERR_ARG), (dict(loader=3), m.ERR_ARG),
+    (dict(lda=63), m.ERR_ARG), (dict(ldb=10), m.ERR_ARG), (dict(ldc=63), m.ERR_ARG),
+    (dict(A=0), m.ERR_ARG), (dict(B=0), m.ERR_ARG), (dict(C=0), m.ERR_ARG),
+    (dict(C=A0), m.ERR_ALIAS), (dict(C=B0 + 4 * 100), m.ERR_ALIAS),
+    (dict(lda=1 << 22), m.ERR_UNSUPPORTED), (dict(M=1 << 20, K=4096), m.ERR_UNSUPPORTED),
+    (dict(A=A0 + 4, loader=1), m.ERR_ARG), (dict(K=62, loader=1), m.ERR_ARG),
+])
+def test_validation_before_any_device_call(kw, want):
+    assert sg(**kw) == want
+
+
+def test_empty_operands_need_no_pointers():
+    # M == 0 or N == 0 is a no-op that touches nothing; NULL is fine there
+    assert m.mgemm_sgemm(0, 5, 5, 0, 5, B0, 5, 0, 5, 2, 1, None) == m.OK
+    assert m.mgemm_sgemm(5, 0, 5, A0, 5, 0, 0, 0, 0, 2, 1, None) == m.OK
+
+
+def test_copy_validation():
+    f = m.mgemm_tile_copy
+    assert f(10, 10, A0, 10, B0, 10, 0, None) == m.ERR_ARG
+    assert f(10, 10, A0, 9, B0, 10, 2, None) == m.ERR_ARG
+    assert f(10, 10, A0, 10, A0 + 40, 10, 2, None) == m.ERR_ALIAS
+    assert f(10, 10, 0, 10, B0, 10, 2, None) == m.ERR_ARG
+    assert f(0, 10, 0, 10, 0, 10, 2, None) == m.OK
+
+
+def test_plan_tiles_loaders_and_lds():
+    p = m.plan(256, 256, 256)
+    assert (p["bm"], p["bn"], p["bk"], p["threads"], p["blocks"]) == (64, 64, 16, 256, 16)
+    assert p["load_bytes"] == 16 and p["slices"] == 16
+    p = m.plan(4096, 4096, 4096, compute="mfma", stages=3)
+    assert (p["bm"], p["blocks"], p["lds_bytes"], p["loads_per_slice"], p["max_vmcnt"]) == (128, 1024, 49152, 4, 4)
+    # ragged, misaligned leading dimensions -> 4-byte loads
+    p = m.plan(4099, 3001, 1537, stages=3, lda=1537, ldb=3001, ldc=3001)
+    assert p["load_bytes"] == 4 and p["bm"] == 128 and p["blocks"] == 33 * 24 and p["slices"] == 97
+    assert p["loads_per_slice"] == 16 and p["max_vmcnt"] == 16
+    # tall-skinny keeps enough blocks with 64 x 64 tiles
+    p = m.plan(16384, 64, 4096)
+    assert p["bm"] == 64 and p["blocks"] == 256
+    # misaligned base
+    st, pl = m.mgemm_plan_sgemm(64, 64, 64, A0 + 4, 64, B0, 64, C0, 64, 2, 1, 0, 0, 0)
+    assert st == m.OK and pl.load_bytes == 4
+    for S in (1, 2, 3):
+        for b in ("64x64", "128x128"):
+            for ld in ("b128", "b32"):
+                assert m.plan(512, 512, 512, stages=S, tile=b, loader=ld)["max_vmcnt"] <= 63
+
+
+def test_lds_per_stage_matches_the_pages_budget():
+    """The day-74 lesson reports ptxas shared memory per block for its 64x64x16
+    kernel; every stage holds one 64x16 A tile and one 16x64 B tile (8 KiB),
+    plus the libcu++ pipeline's own state. Our ring needs no such state, so the
+    page's totals minus ours leave exactly a per-stage-growing remainder."""
+    rows = [l.split() for l in open(os.path.join(ROOT, "tests", "golden", "day74_smem_per_block.txt"))
+            if l.strip() and not l.startswith("#")]
+    page = {int(s): int(b) for s, b in rows}
+    for S in (2, 3):
+        ours = m.plan(512, 512, 512, stages=S)["lds_bytes"]
+        assert ours == S * 8192
+        assert page[S] - ours == 8 + 16 * S  # 8 B header + 16 B per stage
+    assert page[4] - 4 * 8192 == 8 + 16 * 4 and page[5] - 5 * 8192 == 8 + 16 * 5
+
+
+# ---- the ring schedule the kernels execute ---------------------------------
+
+def simulate_piped(events, S, T):
+    """Check an asynchronous-ring trace: every slice issued once in order; a
+    slot is refilled only after a barrier that follows the compute on its
+    previous slice; compute(t) follows a wait that leaves slice t complete and
+    a barrier after it; in flight never exceeds S-1 during compute (S for S=1)."""
+    issued, done = [], set()
+    slot_of = {}
+    slot_busy = {}  # slot -> slice computed-from but not yet released by a barrier
+    last_compute_released = True
+    computed = []
+    waited_since_issue = {}
+    barrier_after_wait = set()
+    for op, a, b in events:
+        if op == 1:  # issue a -> slot b
+            assert a == len(issued), "slices issued out of order"
+            assert 0 <= b < S
+            # slot b must not hold an uncomputed slice or one computed without a barrier since
+            for s, sl in slot_of.items():
+                if sl == b and s not in computed:
+                    raise AssertionError(f"slot {b} refilled before slice {s} was computed")
+            assert slot_busy.get(b) is None, f"slot {b} refilled before a barrier released it"
+            issued.append(a)
+            slot_of[a] = b
+        elif op == 2:  # wait: at most a slices in flight
+            inflight = [s for s in issued if s not in done]
+            keep = inflight[len(inflight) - a:] if a else []
+            for s in inflight:
+                if s not in keep:
+                    done.add(s)
+        elif op == 3:  # barrier
+            for s in list(done):
+                barrier_after_wait.add(s)
+            slot_busy.clear()
+        elif op == 4:  # compute a from slot b
+            assert a == len(computed), "compute out of order"
+            assert a in barrier_after_wait, f"slice {a} computed before wait+barrier"
+            assert slot_of[a] == b
+            inflight = [s for s in issued if s not in done]
+            assert len(inflight) <= max(S - 1, 0)
+            computed.append(a)
+            slot_busy[b] = a
+        else:
+            raise AssertionError(f"unexpected op {op}")
+    assert issued == list(range(T)) and computed == list(range(T))
+
+
+def simulate_sync(events, S, T):
+    """Check a synchronous-ring trace: each slice loaded once, in order, into a
+    register set that is free; stored from the set holding it into the slot it
+    is computed from; a barrier separates store and compute; a slot is
+    overwritten only after a barrier that follows the compute on it."""
+    R = max(S - 1, 1)
+    sets = {}
+    loaded = []
+    slot_holds = {}
+    visible = set()
+    slot_busy = {}
+    computed = []
+    for op, a, b in events:
+        if op == 6:  # load slice a into set b
+            assert a == len(loaded) and 0 <= b < R
+            assert sets.get(b) is None, f"register set {b} reused before its store"
+            sets[b] = a
+            loaded.append(a)
+        elif op == 5:  # store set a -> slot b
+            assert sets.get(a) is not None, "store of an empty register set"
+            assert slot_busy.get(b) is None, f"slot {b} overwritten before a barrier released it"
+            assert slot_holds.get(b) is None or slot_holds[b] in computed, f"slot {b} overwritten before use"
+            s = sets.pop(a)
+            slot_holds[b] = s
+            visible.discard(s)
+            slot_busy[b] = "written"
+        elif op == 3:
+            for sl, s in slot_holds.items():
+                visible.add(s)
+            slot_busy.clear()
+        elif op == 4:
+            assert a == len(computed)
+            assert slot_holds.get(b) == a and a in visible, f"slice {a} not visible in slot {b}"
+            computed.append(a)
+            slot_busy[b] = "read"
+        else:
+            raise AssertionError(op)
+    assert loaded == list(range(T)) and computed == list(range(T))
+
+
+@pytest.mark.parametrize("S", [1, 2, 3])
+@pytest.mark.parametrize("fill", [0, 1])
+def test_ring_schedule(S, fill):
+    for T in list(range(0, 12)) + [31, 40, 97]:
+        ev = m.mgemm_ring_trace(0, S, fill, T)
+        if fill == 1:
+            simulate_piped(ev, S, T)
+            waits = [a for op, a, b in ev if op == 2]
+            assert all(0 <= w <= max(S - 2, 0) for w in waits)
+        else:
+            simulate_sync(ev, S, T)
+    assert m.mgemm_ring_trace(1, S, 1, 5) == m.mgemm_ring_trace(0, S, 1, 5)
+
+
+def test_ring_trace_rejects_bad_arguments():
+    assert m.lib().mgemm_ring_trace(0, 4, 1, 3, None, 0) == m.ERR_ARG
+    assert m.lib().mgemm_ring_trace(1, 2, 0, 3, None, 0) == m.ERR_ARG
+    assert m.lib().mgemm_ring_trace(2, 2, 1, 3, None, 0) == m.ERR_ARG
+
+
+def test_simulators_catch_planted_schedule_bugs():
+    """The checkers above reject the classic ring mistakes."""
+    good = m.mgemm_ring_trace(0, 3, 1, 6)
+    # compute before waiting: drop the first wait
+    bad = list(good)
+    bad.remove(next(e for e in bad if e[0] == 2))
+    with pytest.raises(AssertionError):
+        simulate_piped(bad, 3, 6)
+    # wrong slot index for a compute
+    bad = [(4, a, (b + 1) % 3) if op == 4 and a == 2 else (op, a, b) for op, a, b in good]
+    with pytest.raises(AssertionError):
+        simulate_piped(bad, 3, 6)
+    # refill a slot before the barrier that releases it: swap barrier and issue in one iteration
+    i = next(k for k in range(1, len(good)) if good[k][0] == 1 and good[k - 1][0] == 3 and good[k][1] >= 3)
+    bad = list(good)
+    bad[i - 1], bad[i] = bad[i], bad[i - 1]
+    with pytest.raises(AssertionError):
+        simulate_piped(bad, 3, 6)
+    # sync ring: drop the barrier between store and compute
+    good = m.mgemm_ring_trace(0, 2, 0, 5)
+    bad = list(good)
+    del bad[next(k for k, e in enumerate(bad) if e[0] == 3)]
+    with pytest.raises(AssertionError):
+        simulate_sync(bad, 2, 5)
+
+
+# ---- evidence in our own gfx950 ISA -----------------------------------------
+
+def _kernels(isa):
+    out = {}
+    cur = None
+    for line in isa.splitlines():
+        mm = re.match(r"^(_ZN5mgemm\w+):", line)
+        if mm:
+            cur = mm.group(1)
+            out[cur] = []
+        elif cur is not None:
+            if line.startswith(".Lfunc_end"):
+                cur = None
+            else:
+                out[cur].append(line)
+    return out
+
+
+def _name(cfg, S, piped, W):
+    return f"_ZN5mgemm12sgemm_kernelINS_{len(cfg)}{cfg}ELi{S}ELb{int(piped)}ELi{W}EEEvNS_8GemmArgsE"
+
+
+@pytest.fixture(scope="module")
+def isa():
+    if not os.path.exists(m.ISA_PATH):
+        pytest.skip("ISA not built")
+    return _kernels(open(m.ISA_PATH).read())
+
+
+@pytest.mark.parametrize("cfg", ["CfgValu64", "CfgValu128", "CfgMfma64", "CfgMfma128"])
+def test_isa_fill_instructions(isa, cfg):
+    """Piped kernels fill LDS with buffer_load ... lds and no ds_write; sync
+    kernels fill through VGPRs (ds_write) and have no LDS-direct load."""
+    for S in (1, 2, 3):
+        for W in (16, 4):
+            body = "\n".join(isa[_name(cfg, S, True, W)])
+            width = "dwordx4" if W == 16 else "dword"
+            assert re.search(rf"buffer_load_{width} .* lds", body), (cfg, S, W)
+            assert "ds_write" not in body, (cfg, S, W)
+            sbody = "\n".join(isa[_name(cfg, S, False, W)])
+            assert " lds" not in sbody.replace("lds_", "") or not re.search(r"buffer_load\S* .* lds", sbody)
+            assert "ds_write" in sbody
+            assert "v_pk_fma_f32" not in body and "v_pk_fma_f32" not in sbody
+
+
+@pytest.mark.parametrize("cfg", ["CfgValu64", "CfgValu128", "CfgMfma64", "CfgMfma128"])
+def test_isa_compute_does_not_drain_the_prefetch(isa, cfg):
+    """In the piped S >= 2 kernels no s_waitcnt vmcnt(0) sits between a ring
+    barrier and the arithmetic that follows it: the compute runs while the
+    next slices are still in flight."""
+    op = "v_mfma_f32_32x32x2_f32" if "Mfma" in cfg else "v_fma"
+    for S in (2, 3):
+        for W in (16, 4):
+            lines = isa[_name(cfg, S, True, W)]
+            segs, cur = [], []
+            for l in lines:
+                if "s_barrier" in l:
+                    segs.append(cur)
+                    cur = []
+                else:
+                    cur.append(l)
+            segs.append(cur)
+            compute_segs = [s for s in segs[1:] if any(op in l for l in s)]
+            assert compute_segs, (cfg, S, W)
+            for s in compute_segs:
+                head = []
+                for l in s:
+                    if op in l:
+                        break
+                    head.append(l)
+                assert not any("vmcnt(0)" in l for l in head), (cfg, S, W)
+            if S == 3:
+                body = "\n".join(lines)
+                n = m.plan(1024, 1024, 1024, stages=3, tile="128x128" if "128" in cfg else "64x64",
+                           loader="b128" if W == 16 else "b32")["max_vmcnt"]
+                assert f"s_waitcnt vmcnt({n})" in body, (cfg, W, n)

@@ -1,0 +1,124 @@
+"""Parity at the full benchmark sizes, in the launch configurations the
+benchmark times: sampled rows against the oracle (computed one row at a time),
+and properties that hold at any size (bit identity across fills and stages,
+closed forms). Inputs: A, B ~ U[-1, 1) from the seeded generator."""
+import numpy as np
+import pytest
+import torch
+
+import async_global_shared_amd as m
+import datagen
+from tests.gpu_util import check_bound, same_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_uniform(seed, rows, cols):
+    return datagen.uniform_pm1_torch(seed, rows * cols, device="cuda").view(rows, cols)
+
+
+def _sample_rows(M, n=12):
+    rows = sorted(set([0, 1, M // 3, M // 2, M - 2, M - 1] + list(np.linspace(0, M - 1, n).astype(int))))
+    return np.array(rows)
+
+
+def _host_rows(Ad, rows):
+    return Ad[torch.as_tensor(rows, device=Ad.device)].cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_square_full_size(n):
+    M = N = K = n
+    Ad = _dev_uniform(datagen.SEED_A, M, K)
+    Bd = _dev_uniform(datagen.SEED_B, K, N)
+    # the generator's GPU twin equals the CPU one (integer arithmetic)
+    assert torch.equal(Ad[:2, :100].cpu(), torch.from_numpy(datagen.uniform_pm1(datagen.SEED_A, 2 * K)
+                                                              .reshape(2, K)[:, :100]))
+    B = Bd.cpu().numpy()
+    rows = _sample_rows(M)
+    A_rows = _host_rows(Ad, rows)
+    for compute in ("mfma", "valu"):
+        ref = torch.empty((M, N), device="cuda")
+        m.sgemm(Ad, Bd, ref, stages=3, fill="piped", compute=compute, tile="128x128")
+        torch.cuda.synchronize()
+        C_rows = ref[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+        check_bound(C_rows, A_rows, B, what=f"{n}^3 {compute} piped S=3 (sampled rows)")
+        other = torch.empty_like(ref)
+        variants = [("sync", 1), ("piped", 2)] if compute == "valu" and n == 8192 else \
+            [("sync", 1), ("sync", 2), ("sync", 3), ("piped", 1), ("piped", 2)]
+        for fill, S in variants:
+            other.fill_(float("nan"))
+            m.sgemm(Ad, Bd, other, stages=S, fill=fill, compute=compute, tile="128x128")
+            torch.cuda.synchronize()
+            assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), (n, compute, fill, S)
+        del ref, other
+
+
+def test_ragged_full_size():
+    """M = 4099, N = 3001, K = 1537 with lda = 1537 and ldb = ldc = 3001: no
+    leading dimension is a multiple of 4, so every fill takes 4-byte loads,
+    and the last K slice holds one valid k."""
+    M, N, K = 4099, 3001, 1537
+    Ad = _dev_uniform(datagen.SEED_A, M, K)
+    Bd = _dev_uniform(datagen.SEED_B, K, N)
+    assert m.plan(M, N, K, lda=K, ldb=N, ldc=N)["load_bytes"] == 4
+    B = Bd.cpu().numpy()
+    rows = _sample_rows(M)
+    A_rows = _host_rows(Ad, rows)
+    for compute in ("valu", "mfma"):
+        ref = torch.empty((M, N), device="cuda")
+        m.sgemm(Ad, Bd, ref, stages=3, fill="piped", compute=compute)
+        torch.cuda.synchronize()
+        check_bound(ref[torch.as_tensor(rows, device="cuda")].cpu().numpy(), A_rows, B,
+                    what=f"ragged {compute}")
+        other = torch.empty_like(ref)
+        for fill, S in (("sync", 1), ("piped", 2)):
+            m.sgemm(Ad, Bd, other, stages=S, fill=fill, compute=compute)
+            torch.cuda.synchronize()
+            assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), (compute, fill, S)
+
+
+def test_tall_skinny_full_size():
+    M, N, K = 16384, 64, 4096
+    Ad = _dev_uniform(datagen.SEED_A, M, K)
+    Bd = _dev_uniform(datagen.SEED_B, K, N)
+    B = Bd.cpu().numpy()
+    rows = _sample_rows(M, 24)
+    A_rows = _host_rows(Ad, rows)
+    for compute in ("valu", "mfma"):
+        ref = torch.empty((M, N), device="cuda")
+        m.sgemm(Ad, Bd, ref, stages=3, fill="piped", compute=compute)
+        torch.cuda.synchronize()
+        check_bound(ref[torch.as_tensor(rows, device="cuda")].cpu().numpy(), A_rows, B,
+                    what=f"tall-skinny {compute}")
+        other = torch.empty_like(ref)
+        m.sgemm(Ad, Bd, other, stages=1, fill="sync", compute=compute)
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), compute
+
+
+def test_sentinel_full_size_8192():
+    """A = 1, B[k, j] = floor(k/16): C = 16 T (T-1) / 2 exactly (T = 512,
+    2093056 < 2^24, every partial sum an exact integer), on the whole 8192^3
+    output of the timed configuration."""
+    n = 8192
+    Ad = torch.ones((n, n), device="cuda")
+    Bd = (torch.arange(n, device="cuda", dtype=torch.int64) // 16).to(torch.float32)[:, None].expand(n, n).contiguous()
+    want = 16 * 512 * 511 // 2
+    C = torch.empty((n, n), device="cuda")
+    for compute in ("mfma", "valu"):
+        for fill, S in (("piped", 3), ("piped", 2), ("sync", 1)):
+            C.fill_(float("nan"))
+            m.sgemm(Ad, Bd, C, stages=S, fill=fill, compute=compute, tile="128x128")
+            torch.cuda.synchronize()
+            assert bool(torch.all(C == want)), (compute, fill, S)
+
+
+@pytest.mark.parametrize("S", [2, 3])
+def test_copy_one_gib(S):
+    rows = cols = 16384  # 2^28 fp32 = 1 GiB
+    src = datagen.normal01_torch(datagen.SEED_COPY, rows * cols, device="cuda").view(rows, cols)
+    dst = torch.full_like(src, float("nan"))
+    m.tile_copy(src, dst, stages=S)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.view(torch.int32), src.view(torch.int32))

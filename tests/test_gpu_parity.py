@@ -1,0 +1,264 @@
+"""Parity of the HIP path with the oracle, through the C ABI, on the GPU.
+
+Bars: every GPU result lies within |C - C_ref| <= 4 K 2^-24 (|A||B|)_ij of the
+fp64 oracle; for a fixed (compute, tile) every fill mode, stage count and
+loader width gives bit-identical C ("pipelined_gemm.cu": the piped output must
+be memcmp-equal to the sync one before anything is timed); on inputs whose
+every partial sum is exact the result equals the oracle bit for bit; C cells
+outside M x N are never written; and the tile copy returns its input bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import async_global_shared_amd as m
+import datagen
+import oracle
+from tests.gpu_util import (FILLS, SENTINEL, STAGES, TILES, check_bound, full_rows, out_device, padded_device, run,
+                            same_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(kind, M, N, K, seed=0):
+    A = datagen.matrix(kind, datagen.SEED_A + seed, M, K)
+    B = datagen.matrix(kind, datagen.SEED_B + seed, K, N)
+    return A, B
+
+
+# ---- config: 256^3, 64x64x16 tile, 4x4 micro-tile, sync S=1 vs piped S=2 ------
+
+def test_page_kernel_shape_256():
+    M = N = K = 256
+    A, B = _inputs("uniform", M, N, K)
+    Ad, Bd = padded_device(A), padded_device(B)
+    p = m.plan(M, N, K)
+    assert (p["bm"], p["bn"], p["bk"], p["threads"]) == (64, 64, 16, 256)
+    cs = full_rows(run(Ad, Bd, out_device(M, N), compute="valu", tile="64x64", fill="sync", stages=1))
+    cp = full_rows(run(Ad, Bd, out_device(M, N), compute="valu", tile="64x64", fill="piped", stages=2))
+    check_bound(cs, A, B, what="sync S=1")
+    assert same_bits(cs, cp), "piped S=2 differs from sync S=1"
+
+
+# ---- config: 1024^3, stages 1..3 x {sync, piped}, bit identity --------------------
+
+@pytest.mark.parametrize("compute", ["valu", "mfma"])
+def test_1024_all_stages_and_fills(compute):
+    M = N = K = 1024
+    A, B = _inputs("uniform", M, N, K)
+    Ad, Bd = padded_device(A), padded_device(B)
+    outs = {}
+    for fill in FILLS:
+        for S in STAGES:
+            outs[(fill, S)] = full_rows(run(Ad, Bd, out_device(M, N), compute=compute, tile="auto", fill=fill,
+                                            stages=S))
+    ref = outs[("sync", 1)]
+    worst = check_bound(ref, A, B, what=f"{compute} sync S=1")
+    assert worst <= 1.0
+    for k, v in outs.items():
+        assert same_bits(v, ref), f"{compute} {k} differs from sync S=1"
+
+
+# ---- every variant on ragged shapes, aligned and misaligned layouts -------------
+
+LAYOUTS = {
+    # M, N, K, lda, ldb, ldc, base offsets (A, B, C) in floats
+    "aligned": (300, 260, 200, 200, 260, 260, (0, 0, 0)),
+    "padded_ld": (300, 260, 200, 204, 268, 264, (0, 0, 0)),
+    "misaligned": (301, 259, 203, 207, 263, 267, (1, 3, 2)),
+    "tiny_k": (130, 70, 5, 9, 70, 75, (0, 0, 0)),
+}
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+def test_every_variant_ragged(layout):
+    M, N, K, lda, ldb, ldc, (oa, ob, oc) = LAYOUTS[layout]
+    A, B = _inputs("uniform", M, N, K, seed=10)
+    Ad = padded_device(A, lda, offset=oa)
+    Bd = padded_device(B, ldb, offset=ob)
+    loaders = ["auto", "b32"]
+    for compute, tile in TILES:
+        ref = None
+        for fill in FILLS:
+            for S in STAGES:
+                for ld in loaders:
+                    Cd = out_device(M, N, ldc, offset=oc)
+                    full = full_rows(run(Ad, Bd, Cd, compute=compute, tile=tile, fill=fill, stages=S, loader=ld))
+                    assert np.all(full[:, N:] == SENTINEL), f"{layout} {compute} {tile}: wrote C padding"
+                    C = full[:, :N]
+                    if ref is None:
+                        check_bound(C, A, B, what=f"{layout} {compute} {tile} {fill} S={S} {ld}")
+                        ref = C
+                    else:
+                        assert same_bits(C, ref), f"{layout} {compute} {tile} {fill} S={S} {ld} != first variant"
+
+
+def test_b128_and_b32_loaders_agree_when_both_apply():
+    M, N, K = 384, 256, 320
+    A, B = _inputs("uniform", M, N, K, seed=20)
+    Ad, Bd = padded_device(A), padded_device(B)
+    for compute, tile in TILES:
+        a = full_rows(run(Ad, Bd, out_device(M, N), compute=compute, tile=tile, fill="piped", stages=3,
+                          loader="b128"))
+        b = full_rows(run(Ad, Bd, out_device(M, N), compute=compute, tile=tile, fill="piped", stages=3,
+                          loader="b32"))
+        assert same_bits(a, b), (compute, tile)
+
+
+# ---- exactness pins ---------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(200, 136, 520), (1024, 1024, 1024)])
+def test_coarse_grid_is_exact_for_every_variant(shape):
+    """Inputs on the 2^-4 grid make every fp32 partial sum exact, so every
+    variant, MFMA included, must equal the oracle rounded to fp32, bit for bit."""
+    M, N, K = shape
+    A, B = _inputs("coarse", M, N, K, seed=30)
+    want = oracle.gemm_f64(A, B).astype(np.float32)
+    Ad, Bd = padded_device(A), padded_device(B)
+    for compute, tile in TILES:
+        for fill, S in (("sync", 1), ("piped", 2), ("piped", 3)):
+            C = full_rows(run(Ad, Bd, out_device(M, N), compute=compute, tile=tile, fill=fill, stages=S))
+            assert same_bits(C, want), (shape, compute, tile, fill, S)
+
+
+@pytest.mark.parametrize("K", [1000, 1537, 16, 17])
+def test_slice_sentinels(K):
+    """A = 1, B[k, j] = floor(k/16) (and the mirror) give C = 16 T(T-1)/2 + rT
+    exactly; a slice computed from the wrong ring slot changes the sum."""
+    T, r = K // 16, K % 16
+    want = np.float32(16 * T * (T - 1) // 2 + r * T)
+    M, N = 192, 160
+    pairs = [(np.ones((M, K), np.float32), datagen.slice_sentinel(K, N, axis=0)),
+             (datagen.slice_sentinel(M, K, axis=1), np.ones((K, N), np.float32))]
+    for A, B in pairs:
+        Ad, Bd = padded_device(A), padded_device(B)
+        for compute, tile in TILES:
+            for fill in FILLS:
+                for S in STAGES:
+                    C = full_rows(run(Ad, Bd, out_device(M, N), compute=compute, tile=tile, fill=fill, stages=S))
+                    assert np.all(C == want), (K, compute, tile, fill, S)
+
+
+def test_closed_forms_identity_and_permutation():
+    M = K = 192
+    N = 136
+    B = datagen.matrix("uniform", 41, K, N)
+    I = np.eye(M, dtype=np.float32)
+    perm = np.random.default_rng(5).permutation(M)
+    P = np.zeros((M, M), np.float32)
+    P[np.arange(M), perm] = 1.0
+    Bd = padded_device(B)
+    for A, want in ((I, B), (P, B[perm])):
+        Ad = padded_device(A)
+        for compute, tile in TILES:
+            for fill, S in (("sync", 1), ("piped", 3)):
+                C = full_rows(run(Ad, Bd, out_device(M, N), compute=compute, tile=tile, fill=fill, stages=S))
+                C = np.where(C == 0, 0.0, C).astype(np.float32)  # -0 and +0 compare equal
+                assert np.array_equal(C, want), (compute, tile, fill, S)
+
+
+def test_page_input_pattern_relative_tolerance():
+    """The day-74 program's own inputs and its relative 1e-4 check."""
+    for n in (512, 1024):
+        A = datagen.page_pattern_a(n * n).reshape(n, n)
+        B = datagen.page_pattern_b(n * n).reshape(n, n)
+        ref = oracle.gemm_f64(A, B)
+        Ad, Bd = padded_device(A), padded_device(B)
+        for compute in ("valu", "mfma"):
+            C = full_rows(run(Ad, Bd, out_device(n, n), compute=compute, tile="auto", fill="piped", stages=2))
+            scale = np.where(ref == 0, 1.0, np.abs(ref))
+            assert np.all(np.abs(C - ref) <= 1e-4 * scale), (n, compute)
+            check_bound(C, A, B, what=f"page pattern {n} {compute}")
+
+
+# ---- edge cases ---------------------------------------------------------------------
+
+def test_k_zero_writes_zeros_only_inside():
+    M, N, ldc = 70, 50, 53
+    Ad = torch.empty((M, 0), device="cuda")
+    Bd = torch.empty((0, N), device="cuda")
+    Cd = out_device(M, N, ldc)
+    m.sgemm(Ad, Bd, Cd, stages=2, fill="piped")
+    torch.cuda.synchronize()
+    full = full_rows(Cd)
+    assert np.all(full[:, :N] == 0) and not np.any(np.signbit(full[:, :N]))
+    assert np.all(full[:, N:] == SENTINEL)
+
+
+def test_empty_m_or_n_is_a_noop():
+    Cd = out_device(4, 4)
+    A = torch.ones((0, 8), device="cuda")
+    B = torch.ones((8, 4), device="cuda")
+    m.sgemm(A, B, torch.empty((0, 4), device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(Cd == SENTINEL)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 1000, 37), (999, 1, 64), (65, 65, 15), (2, 3, 1)])
+def test_small_and_degenerate(shape):
+    M, N, K = shape
+    A, B = _inputs("uniform", M, N, K, seed=50)
+    Ad, Bd = padded_device(A), padded_device(B)
+    for compute, tile in TILES:
+        ref = None
+        for fill in FILLS:
+            for S in STAGES:
+                C = full_rows(run(Ad, Bd, out_device(M, N), compute=compute, tile=tile, fill=fill, stages=S))
+                if ref is None:
+                    check_bound(C, A, B, what=f"{shape} {compute} {tile}")
+                    ref = C
+                assert same_bits(C, ref), (shape, compute, tile, fill, S)
+
+
+def test_errors_through_the_abi_on_device():
+    A = torch.ones((64, 64), device="cuda")
+    B = torch.ones((64, 64), device="cuda")
+    with pytest.raises(m.MgemmError) as e:
+        m.sgemm(A, B, A)  # C overlaps A
+    assert e.value.status == m.ERR_ALIAS
+    Bm = torch.ones(64 * 64 + 1, device="cuda")[1:].view(64, 64)  # misaligned base
+    with pytest.raises(m.MgemmError) as e:
+        m.sgemm(A, Bm, loader="b128")
+    assert e.value.status == m.ERR_ARG
+
+
+def test_runs_on_a_non_default_stream():
+    M = N = K = 512
+    A, B = _inputs("uniform", M, N, K, seed=60)
+    Ad, Bd = padded_device(A), padded_device(B)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Cd = out_device(M, N)
+        m.sgemm(Ad, Bd, Cd, stages=3, fill="piped", compute="mfma")
+    s.synchronize()
+    check_bound(full_rows(Cd), A, B, what="side stream")
+
+
+# ---- tile copy ---------------------------------------------------------------------
+
+def test_copy_page_example_pattern():
+    """The TVM cp.async page copies (arange(4096) % 97) as 128 x 32 through
+    shared memory and asserts array equality; the same pattern in fp32."""
+    x = (np.arange(4096) % 97).astype(np.float32).reshape(128, 32)
+    src = padded_device(x)
+    for S in STAGES:
+        dst = out_device(128, 32)
+        m.tile_copy(src, dst, stages=S)
+        torch.cuda.synchronize()
+        assert same_bits(full_rows(dst), x)
+
+
+@pytest.mark.parametrize("case", [
+    (1000, 777, 781, 790, 0, 0), (64, 64, 64, 64, 0, 0), (130, 200, 200, 204, 1, 0), (5, 3, 3, 3, 0, 1),
+    (257, 1024, 1024, 1024, 0, 0)])
+def test_copy_ragged(case):
+    rows, cols, lds, ldd, os_, od = case
+    x = datagen.matrix("normal", datagen.SEED_COPY, rows, cols)
+    src = padded_device(x, lds, offset=os_)
+    for S in STAGES:
+        dst = out_device(rows, cols, ldd, offset=od)
+        m.tile_copy(src, dst, stages=S)
+        torch.cuda.synchronize()
+        full = full_rows(dst)
+        assert same_bits(np.ascontiguousarray(full[:, :cols]), x), (case, S)
+        assert np.all(full[:, cols:] == SENTINEL), (case, S)
