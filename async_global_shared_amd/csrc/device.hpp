@@ -478,11 +478,17 @@ __global__ void __launch_bounds__(kThreads) zero_kernel(float *C, int M, int N, 
 
 // ---- pipelined tile copy -----------------------------------------------------------
 //
-// dst = src through an S-slot ring of 64 x 64 fp32 LDS tiles. Waves 0-1 only
-// fill (asynchronous global -> LDS), waves 2-3 only drain (LDS -> VGPR ->
-// global). Keeping stores out of the filling waves keeps their vmcnt a pure
-// count of their own fills, so the ring's waits are exact. Block b copies
-// tiles b, b + G, b + 2G, ... (G = grid size).
+// dst = src through an S-slot ring of 64 x 64 fp32 LDS tiles. Of the block's
+// 8 waves, waves 0-3 only fill (asynchronous global -> LDS, non-temporal:
+// the data is used once) and waves 4-7 only drain (LDS -> VGPR -> global,
+// non-temporal stores). Keeping stores out of the filling waves keeps their
+// vmcnt a pure count of their own fills, so the ring's waits are exact.
+// Block b copies tiles b, b + G, b + 2G, ... (G = grid size).
+constexpr int kCopyWaves = 8;
+constexpr int kCopyFillWaves = 4;
+constexpr int kCopyThreads = 64 * kCopyWaves;
+constexpr int kAuxNonTemporal = 2; // buffer load cache-policy bit: streaming
+
 struct CopyArgs {
     const float *src;
     float *dst;
@@ -496,7 +502,7 @@ using CopyLayout = Layout<64, 64, SwzNone>;
 template <int W, bool VST>
 struct CopyOps {
     static constexpr int SLOT = CopyLayout::BYTES;
-    static constexpr int PW = 2; // filling waves
+    static constexpr int PW = kCopyFillWaves;
     using OP = Operand<CopyLayout, W, PW>;
     CopyArgs a;
     OP op;
@@ -519,7 +525,7 @@ struct CopyOps {
 #pragma unroll
         for (int i = 0; i < OP::U; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t *)(base + OP::lds_off(i, wave)), W,
-                                                      op.voff(i, a.rows - r0, a.cols - c0), 0, 0, 0);
+                                                      op.voff(i, a.rows - r0, a.cols - c0), 0, 0, kAuxNonTemporal);
     }
     template <int P>
     __device__ void wait() {
@@ -533,8 +539,10 @@ struct CopyOps {
         int r0, c0;
         coords(t, r0, c0);
         const unsigned char *base = smem + slot * SLOT;
-        const int cw = wave - PW; // drains chunk rows 32cw .. 32cw+31
-        constexpr int PER = CopyLayout::CHUNKS / (64 * PW);
+        constexpr int CW = kCopyWaves - PW;
+        static_assert(CopyLayout::CHUNKS % (64 * CW) == 0, "whole chunks per draining wave");
+        constexpr int PER = CopyLayout::CHUNKS / (64 * CW);
+        const int cw = wave - PW; // drains chunk positions [cw*PER*64, (cw+1)*PER*64)
         f32x4 v[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j)
@@ -561,7 +569,7 @@ struct CopyOps {
 };
 
 template <int S, int W, bool VST>
-__global__ void __launch_bounds__(kThreads) tile_copy_kernel(CopyArgs a) {
+__global__ void __launch_bounds__(kCopyThreads) tile_copy_kernel(CopyArgs a) {
     using Ops = CopyOps<W, VST>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[S * Ops::SLOT];
     Ops ops;

@@ -169,9 +169,9 @@ const void *copy_kernel(int S, int W, bool vst) {
     }
 }
 
-int launch(const void *fn, int blocks, void *arg, hipStream_t stream) {
+int launch(const void *fn, int blocks, void *arg, hipStream_t stream, int threads = kThreads) {
     void *args[] = {arg};
-    const hipError_t e = hipLaunchKernel(fn, dim3(blocks), dim3(kThreads), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(fn, dim3(blocks), dim3(threads), args, 0, stream);
     return e == hipSuccess ? MGEMM_OK : MGEMM_ERR_LAUNCH;
 }
 
@@ -308,14 +308,14 @@ int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, f
     std::atomic<int> &oc = occ_cache[stages - 1][W == 16][vst];
     int occ = oc.load(std::memory_order_relaxed);
     if (occ == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kThreads, 0) != hipSuccess || occ < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kCopyThreads, 0) != hipSuccess || occ < 1)
             occ = 1;
         oc.store(occ, std::memory_order_relaxed);
     }
     const int64_t resident = (int64_t)occ * g_cus[dev].load(std::memory_order_relaxed);
     const int blocks = (int)std::min<int64_t>(ntiles, resident > 0 ? resident : 256);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    return launch(fn, blocks, &a, s);
+    return launch(fn, blocks, &a, s, kCopyThreads);
 }
 
 int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *events, int cap) {

@@ -27,6 +27,50 @@ if ROOT not in sys.path:
 METRIC = "FP32 GEMM GFLOP/s + % FP32 peak at 4096³/8192³; piped/sync speedup; copy GB/s"
 PEAK_FP32_TFLOPS = 157.3   # MI355X dense FP32 (MFMA and packed vector), AMD spec
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, AMD spec
+# The 1 GiB fp32 array in 64x64 tiles, read two ways: as a 16384 x 16384
+# matrix (each tile row is 256 contiguous bytes, rows 64 KiB apart) and as a
+# 4194304 x 64 matrix (each tile is 16 KiB of contiguous memory).
+COPY_VIEWS = ((16384, 16384), (4194304, 64))
+
+
+KERNEL_SOURCES = ("async_global_shared_amd/csrc/device.hpp", "async_global_shared_amd/csrc/ring.h",
+                  "async_global_shared_amd/csrc/mgemm.hip")
+COUNTERS_FILE = "profiles/counters_gemm8192_and_copy1GiB.txt"
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel and launch sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel_name: str, grid: int):
+    """HBM bytes per launch of `kernel_name` from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the calibration copy),
+    or None when the summary is missing or the kernel sources changed since."""
+    path = os.path.join(ROOT, COUNTERS_FILE)
+    if not os.path.exists(path):
+        return None
+    section, vals, top = None, {}, {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("["):
+            section = line[1:-1]
+            continue
+        k, _, v = line.partition("=")
+        (vals.setdefault(section, {}) if section else top)[k] = v
+    if top.get("kernel_src_sha256") != kernel_source_hash():
+        return None
+    sec = vals.get(f"{kernel_name} grid={grid}")
+    if not sec or "hbm_bytes_per_launch" not in sec:
+        return None
+    return float(sec["hbm_bytes_per_launch"])
 
 
 def parse():
@@ -35,11 +79,45 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--size", type=int, default=8192)
-    p.add_argument("--stages", type=int, default=3)
+    p.add_argument("--stages", type=int, default=2)
     p.add_argument("--compute", default="mfma", choices=["mfma", "valu"])
     p.add_argument("--no-extra", action="store_true", help="skip the tables after the timed region")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    p.add_argument("--profile", action="store_true",
+                   help="only run a few launches of the timed GEMM, the 1 GiB tile copy (3 stages) and a plain "
+                        "1 GiB device copy (the calibration kernel for hardware byte counters), for rocprofv3")
     return p.parse_args()
+
+
+def profile_mode(args):
+    """Launches for counter collection, `steps` of each, no timing: the timed
+    GEMM, its VALU twin, the 1 GiB tile copy in both array views, and a plain
+    1 GiB device copy (the calibration kernel for hardware byte counters)."""
+    import torch
+
+    import async_global_shared_amd as m
+    import datagen
+    n = args.size
+    Ad = datagen.uniform_pm1_torch(datagen.SEED_A, n * n, device="cuda").view(n, n)
+    Bd = datagen.uniform_pm1_torch(datagen.SEED_B, n * n, device="cuda").view(n, n)
+    Cd = torch.empty((n, n), device="cuda")
+    for compute in (args.compute, "valu" if args.compute == "mfma" else "mfma"):
+        for _ in range(args.steps):
+            m.sgemm(Ad, Bd, Cd, stages=args.stages, fill="piped", compute=compute, tile="128x128")
+        torch.cuda.synchronize()
+        print(f"profile: {args.steps} x sgemm {n}^3 {compute} piped S={args.stages}", flush=True)
+    del Ad, Bd, Cd
+    src = datagen.normal01_torch(datagen.SEED_COPY, 1 << 28, device="cuda")
+    dst = torch.empty_like(src)
+    for shape in COPY_VIEWS:
+        for _ in range(args.steps):
+            m.tile_copy(src.view(*shape), dst.view(*shape), stages=3)
+        torch.cuda.synchronize()
+        print(f"profile: {args.steps} x tile_copy 1 GiB as {shape[0]}x{shape[1]} S=3", flush=True)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"profile: {args.steps} x plain device copy 1 GiB (calibration: 2^30 B read, 2^30 B written)", flush=True)
 
 
 def timed_launches(fn, warmup=3, runs=10, repeats=1):
@@ -67,8 +145,11 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the GEMM would shard by C row bands; see DESIGN.md)", file=sys.stderr)
+              "(the GEMM would shard by row bands of C, one band per GPU, with B broadcast)", file=sys.stderr)
         sys.exit(2)
+    if args.profile:
+        profile_mode(args)
+        return
 
     import numpy as np
     import torch
@@ -146,7 +227,10 @@ def main():
                    "tile": "128x128"},
         "roofline": {"bound": "mfma" if args.compute == "mfma" else "alu",
                      "achieved": round(achieved_tflops, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
+                     "traffic": measured_traffic(
+                         f"void mgemm::sgemm_kernel<mgemm::Cfg{'Mfma' if args.compute == 'mfma' else 'Valu'}128, "
+                         f"{args.stages}, true, 16>(mgemm::GemmArgs)", plan["blocks"] * plan["threads"])},
         "cpu_baseline": cpu,
         "extra": extra,
     }
@@ -157,8 +241,9 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
     """Stage/fill table (GFLOP/s, speedups), VALU variant, tile copy GB/s."""
     res = {}
     gemm = {}
-    for n in (4096, 8192):
-        if n == 8192:
+    big = Ad8.shape[0]
+    for n in sorted({min(4096, big), big}):
+        if n == big:
             A, B, C = Ad8, Bd8, Cd8
         else:
             A, B, C = Ad8[:n, :n].contiguous(), Bd8[:n, :n].contiguous(), torch.empty((n, n), device="cuda")
@@ -167,7 +252,7 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
         for compute in ("mfma", "valu"):
             for fill in ("sync", "piped"):
                 for S in (1, 2, 3):
-                    if compute == "valu" and n == 8192 and (fill, S) not in (("sync", 1), ("piped", 2), ("piped", 3)):
+                    if compute == "valu" and n > 4096 and (fill, S) not in (("sync", 1), ("piped", 2), ("piped", 3)):
                         continue
                     t = timed_launches(lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute,
                                                        tile="128x128"), repeats=3)
@@ -185,19 +270,24 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
                 if s and p:
                     p["speedup_vs_sync_same_S"] = round(s["ms"] / p["ms"], 3)
         gemm[str(n)] = row
-        if n != 8192:
+        if n != big:
             del A, B, C
     res["gemm"] = gemm
     # tile copy: 1 GiB fp32 ~ N(0,1), 64x64 tiles, 2 x bytes moved
-    rows = cols = 16384
-    src = datagen.normal01_torch(datagen.SEED_COPY, rows * cols, device="cuda").view(rows, cols)
+    n_el = 1 << 28
+    src = datagen.normal01_torch(datagen.SEED_COPY, n_el, device="cuda")
     dst = torch.empty_like(src)
-    nbytes = 2.0 * src.numel() * 4
+    nbytes = 2.0 * n_el * 4
     copy = {}
-    for S in (1, 2, 3):
-        t = timed_launches(lambda: m.tile_copy(src, dst, stages=S), repeats=3)
-        copy[f"S{S}"] = {"ms": round(t["ms_median"], 4), "GBps": round(nbytes / (t["ms_median"] * 1e-3) / 1e9, 1)}
-        copy[f"S{S}"]["pct_hbm_peak"] = round(100 * copy[f"S{S}"]["GBps"] / PEAK_HBM_GBS, 2)
+    for shape in COPY_VIEWS:
+        view = f"{shape[0]}x{shape[1]}"
+        for S in (1, 2, 3):
+            t = timed_launches(lambda: m.tile_copy(src.view(*shape), dst.view(*shape), stages=S), repeats=3)
+            gbs = nbytes / (t["ms_median"] * 1e-3) / 1e9
+            copy[f"{view}_S{S}"] = {"ms": round(t["ms_median"], 4), "GBps": round(gbs, 1),
+                                    "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
+        if not torch.equal(src, dst):
+            raise SystemExit("tile copy changed bytes")
     t = timed_launches(lambda: dst.copy_(src), repeats=3)
     copy["torch_copy_context"] = {"ms": round(t["ms_median"], 4),
                                   "GBps": round(nbytes / (t["ms_median"] * 1e-3) / 1e9, 1)}

@@ -13,9 +13,9 @@
  *    matmulCpu): the tile shapes, the per-thread float4 fill, the lookahead
  *    loop that keeps up to kStages fetches in flight, and the reference.
  *  - "A study on CUDA async memcpy" (section "async-group based approach"):
- *    waiting "until at most N of the most recent groups are in flight", which
- *    this library realises per wave with s_waitcnt vmcnt(N) and per block with
- *    s_barrier.
+ *    a wait that returns once no more than N of the thread's newest copy
+ *    groups are still outstanding; this library realises it per wave with
+ *    s_waitcnt vmcnt(N) and per block with s_barrier.
  *  - "cp.async" (TVM TIRx, section "Predication is different from zero fill"):
  *    out-of-range parts of a tile are filled with zeros, never left unwritten.
  *
