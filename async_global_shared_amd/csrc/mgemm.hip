@@ -59,7 +59,8 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
         return MGEMM_ERR_ARG;
     if (stages < 1 || stages > 3 || (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED) ||
         (compute != MGEMM_COMPUTE_VALU && compute != MGEMM_COMPUTE_MFMA) || tile < MGEMM_TILE_AUTO ||
-        tile > MGEMM_TILE_128x128 || loader < MGEMM_LOADER_AUTO || loader > MGEMM_LOADER_B32)
+        tile > MGEMM_TILE_256x128 || loader < MGEMM_LOADER_AUTO || loader > MGEMM_LOADER_B32 ||
+        (tile == MGEMM_TILE_256x128 && compute != MGEMM_COMPUTE_MFMA))
         return MGEMM_ERR_ARG;
     int st;
     if ((st = check_matrix(A, M, K, lda)) != MGEMM_OK || (st = check_matrix(B, K, N, ldb)) != MGEMM_OK ||
@@ -89,24 +90,25 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
         const int64_t nb128 = ((M + 127) / 128) * ((N + 127) / 128);
         tile = nb128 >= kAutoBigTileBlocks ? MGEMM_TILE_128x128 : MGEMM_TILE_64x64;
     }
-    const int b = tile == MGEMM_TILE_128x128 ? 128 : 64;
+    const int bm = tile == MGEMM_TILE_256x128 ? 256 : tile == MGEMM_TILE_128x128 ? 128 : 64;
+    const int bn = tile == MGEMM_TILE_64x64 ? 64 : 128;
     mgemm_plan_t p;
     std::memset(&p, 0, sizeof p);
     p.compute = compute;
     p.tile = tile;
-    p.bm = b;
-    p.bn = b;
+    p.bm = bm;
+    p.bn = bn;
     p.bk = kBK;
     p.threads = kThreads;
-    p.blocks = (int)(((M + b - 1) / b) * ((N + b - 1) / b));
+    p.blocks = (int)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
     p.load_bytes = W;
     p.slices = (int)((K + kBK - 1) / kBK);
     p.stages = stages;
     p.fill_mode = fill;
-    p.lds_bytes = stages * (b * kBK + kBK * b) * 4;
+    p.lds_bytes = stages * (bm * kBK + kBK * bn) * 4;
     // one 64-lane instruction moves 64*W bytes; a slice of both operands is
-    // 2*b*16*4 bytes, shared by the 4 waves
-    p.loads_per_slice = (2 * b * kBK * 4) / (64 * W) / kWaves;
+    // (bm+bn)*16*4 bytes, shared by the 4 waves
+    p.loads_per_slice = ((bm + bn) * kBK * 4) / (64 * W) / kWaves;
     p.max_vmcnt = fill == MGEMM_FILL_PIPED ? (stages >= 3 ? (stages - 2) * p.loads_per_slice : 0) : 0;
     if (pl)
         *pl = p;
@@ -262,6 +264,8 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     if (compute == MGEMM_COMPUTE_VALU)
         fn = p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgValu128>(stages, piped, p.load_bytes)
                                           : gemm_kernel<CfgValu64>(stages, piped, p.load_bytes);
+    else if (p.tile == MGEMM_TILE_256x128)
+        fn = gemm_kernel<CfgMfma256x128>(stages, piped, p.load_bytes);
     else
         fn = p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgMfma128>(stages, piped, p.load_bytes)
                                           : gemm_kernel<CfgMfma64>(stages, piped, p.load_bytes);

@@ -55,6 +55,7 @@ extern "C" {
 #define MGEMM_TILE_AUTO 0
 #define MGEMM_TILE_64x64 1   /* VALU: 4x4 micro-tile per thread (the pages' shape) */
 #define MGEMM_TILE_128x128 2 /* VALU: 8x8 micro-tile; MFMA: 2x2 32x32 tiles per wave */
+#define MGEMM_TILE_256x128 3 /* MFMA only: 4x2 32x32 tiles per wave (BM 256, BN 128) */
 
 /* loader: width of each lane's global load (results never depend on it). */
 #define MGEMM_LOADER_AUTO 0 /* 16 B when bases, ld and extents allow, else 4 B */
@@ -117,7 +118,7 @@ int mgemm_version(void);
  */
 typedef struct mgemm_plan {
     int compute;       /* MGEMM_COMPUTE_* */
-    int tile;          /* MGEMM_TILE_64x64 or MGEMM_TILE_128x128 */
+    int tile;          /* MGEMM_TILE_64x64, _128x128 or _256x128 */
     int bm, bn, bk;    /* block tile and K slice */
     int threads;       /* per block */
     int blocks;        /* 1-D grid */

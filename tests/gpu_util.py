@@ -12,7 +12,7 @@ DEV = torch.device("cuda:0")
 SENTINEL = -12345.0
 
 # (compute, tile) pairs, each with its own shared compute tile
-TILES = [("valu", "64x64"), ("valu", "128x128"), ("mfma", "64x64"), ("mfma", "128x128")]
+TILES = [("valu", "64x64"), ("valu", "128x128"), ("mfma", "64x64"), ("mfma", "128x128"), ("mfma", "256x128")]
 FILLS = ["sync", "piped"]
 STAGES = [1, 2, 3]
 

@@ -42,7 +42,7 @@ def sg(M=64, N=64, K=64, A=A0, lda=None, B=B0, ldb=None, C=C0, ldc=None, stages=
 @pytest.mark.parametrize("kw,want", [
     (dict(M=-1), m.ERR_ARG), (dict(N=-1), m.ERR_ARG), (dict(K=-1), m.ERR_ARG),
     (dict(stages=0), m.ERR_ARG), (dict(stages=4), m.ERR_ARG), (dict(fill=2), m.ERR_ARG),
-    (dict(compute=2), m.ERR_ARG), (dict(tile=3), m.ERR_ARG), (dict(loader=3), m.ERR_ARG),
+    (dict(compute=2), m.ERR_ARG), (dict(tile=4), m.ERR_ARG), (dict(tile=3, compute=0), m.ERR_ARG), (dict(loader=3), m.ERR_ARG),
     (dict(lda=63), m.ERR_ARG), (dict(ldb=10), m.ERR_ARG), (dict(ldc=63), m.ERR_ARG),
     (dict(A=0), m.ERR_ARG), (dict(B=0), m.ERR_ARG), (dict(C=0), m.ERR_ARG),
     (dict(C=A0), m.ERR_ALIAS), (dict(C=B0 + 4 * 100), m.ERR_ALIAS),
