@@ -63,10 +63,12 @@ def lib():
         L.mgemm_plan_sgemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci,
                                        ctypes.POINTER(Plan)]
         L.mgemm_ring_trace.argtypes = [ci, ci, ci, ci, ctypes.POINTER(ctypes.c_int), ci]
+        L.mgemm_blocks_per_cu.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci,
+                                          ctypes.POINTER(ctypes.c_int)]
         L.mgemm_status_string.argtypes = [ci]
         L.mgemm_status_string.restype = ctypes.c_char_p
         for f in (L.mgemm_sgemm, L.mgemm_sgemm_ex, L.mgemm_tile_copy, L.mgemm_plan_sgemm,
-                  L.mgemm_ring_trace, L.mgemm_version):
+                  L.mgemm_ring_trace, L.mgemm_version, L.mgemm_blocks_per_cu):
             f.restype = ci
         _lib = L
     return _lib
@@ -100,6 +102,14 @@ def mgemm_plan_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute
     st = lib().mgemm_plan_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader,
                                 ctypes.byref(p))
     return st, p
+
+
+def mgemm_blocks_per_cu(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader):
+    """(status, resident blocks per CU) of the kernel that would be launched."""
+    out = ctypes.c_int(0)
+    st = lib().mgemm_blocks_per_cu(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader,
+                                   ctypes.byref(out))
+    return st, out.value
 
 
 def mgemm_ring_trace(kind: int, stages: int, fill_mode: int, slices: int):
@@ -166,6 +176,15 @@ def tile_copy(src, dst=None, *, stages: int = 3, stream=None):
     if st != OK:
         raise MgemmError(st, "mgemm_tile_copy")
     return dst
+
+
+def blocks_per_cu(M, N, K, *, stages=2, fill="piped", compute="valu", tile="auto", loader="auto"):
+    """Resident blocks per CU of the kernel for this problem (aligned layout)."""
+    st, n = mgemm_blocks_per_cu(M, N, K, 0x10000, K, 0x40000000, N, 0x80000000, N, stages, _FILL[fill],
+                                _COMPUTE[compute], _TILE[tile], _LOADER[loader])
+    if st != OK:
+        raise MgemmError(st, "mgemm_blocks_per_cu")
+    return n
 
 
 def plan(M, N, K, *, stages=2, fill="piped", compute="valu", tile="auto", loader="auto",

@@ -317,10 +317,13 @@ __device__ inline void block_tile(int bid, int gm, int gn, int &tm, int &tn) {
 
 // ---- waits and barriers --------------------------------------------------------
 
+// s_waitcnt vmcnt(N). The counter field is 6 bits: a request above 63 waits
+// for 63, i.e. for more completions than asked, which stays correct.
 template <int N>
 __device__ inline void wait_vm() {
-    static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    static_assert(N >= 0, "vmcnt");
+    constexpr int n = N < 63 ? N : 63;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
 }
 // Block barrier after this wave's LDS reads and writes have completed.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

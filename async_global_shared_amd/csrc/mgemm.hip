@@ -9,6 +9,7 @@
 // same refusals become status codes returned before any work is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -57,7 +58,8 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
               mgemm_plan_t *pl) {
     if (M < 0 || N < 0 || K < 0)
         return MGEMM_ERR_ARG;
-    if (stages < 1 || stages > 3 || (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED) ||
+    if (stages < 1 || stages > kMaxPipedStages || (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED) ||
+        (fill == MGEMM_FILL_SYNC && stages > kMaxSyncStages) ||
         (compute != MGEMM_COMPUTE_VALU && compute != MGEMM_COMPUTE_MFMA) || tile < MGEMM_TILE_AUTO ||
         tile > MGEMM_TILE_256x128 || loader < MGEMM_LOADER_AUTO || loader > MGEMM_LOADER_B32 ||
         (tile == MGEMM_TILE_256x128 && compute != MGEMM_COMPUTE_MFMA))
@@ -109,7 +111,7 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
     // one 64-lane instruction moves 64*W bytes; a slice of both operands is
     // (bm+bn)*16*4 bytes, shared by the 4 waves
     p.loads_per_slice = ((bm + bn) * kBK * 4) / (64 * W) / kWaves;
-    p.max_vmcnt = fill == MGEMM_FILL_PIPED ? (stages >= 3 ? (stages - 2) * p.loads_per_slice : 0) : 0;
+    p.max_vmcnt = fill == MGEMM_FILL_PIPED ? std::min(63, std::max(0, stages - 2) * p.loads_per_slice) : 0;
     if (pl)
         *pl = p;
     return MGEMM_OK;
@@ -138,23 +140,26 @@ int current_device(int *dev) {
 // ---- kernel tables ----------------------------------------------------------------
 
 template <class Cfg, int S, int W>
-constexpr const void *gk(bool piped) {
-    return piped ? (const void *)&sgemm_kernel<Cfg, S, true, W> : (const void *)&sgemm_kernel<Cfg, S, false, W>;
+const void *gk(bool piped) {
+    if constexpr (S <= kMaxSyncStages)
+        if (!piped)
+            return (const void *)&sgemm_kernel<Cfg, S, false, W>;
+    return (const void *)&sgemm_kernel<Cfg, S, true, W>;
+}
+template <class Cfg, int W>
+const void *gemm_kernel_w(int S, bool piped) {
+    switch (S) {
+    case 1: return gk<Cfg, 1, W>(piped);
+    case 2: return gk<Cfg, 2, W>(piped);
+    case 3: return gk<Cfg, 3, W>(piped);
+    case 4: return gk<Cfg, 4, W>(piped);
+    case 5: return gk<Cfg, 5, W>(piped);
+    default: return gk<Cfg, 6, W>(piped);
+    }
 }
 template <class Cfg>
 const void *gemm_kernel(int S, bool piped, int W) {
-    if (W == 16) {
-        switch (S) {
-        case 1: return gk<Cfg, 1, 16>(piped);
-        case 2: return gk<Cfg, 2, 16>(piped);
-        default: return gk<Cfg, 3, 16>(piped);
-        }
-    }
-    switch (S) {
-    case 1: return gk<Cfg, 1, 4>(piped);
-    case 2: return gk<Cfg, 2, 4>(piped);
-    default: return gk<Cfg, 3, 4>(piped);
-    }
+    return W == 16 ? gemm_kernel_w<Cfg, 16>(S, piped) : gemm_kernel_w<Cfg, 4>(S, piped);
 }
 
 template <int S>
@@ -167,8 +172,22 @@ const void *copy_kernel(int S, int W, bool vst) {
     switch (S) {
     case 1: return ck<1>(W, vst);
     case 2: return ck<2>(W, vst);
-    default: return ck<3>(W, vst);
+    case 3: return ck<3>(W, vst);
+    case 4: return ck<4>(W, vst);
+    case 5: return ck<5>(W, vst);
+    default: return ck<6>(W, vst);
     }
+}
+
+const void *select_gemm(const mgemm_plan_t &p) {
+    const bool piped = p.fill_mode == MGEMM_FILL_PIPED;
+    if (p.compute == MGEMM_COMPUTE_VALU)
+        return p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgValu128>(p.stages, piped, p.load_bytes)
+                                            : gemm_kernel<CfgValu64>(p.stages, piped, p.load_bytes);
+    if (p.tile == MGEMM_TILE_256x128)
+        return gemm_kernel<CfgMfma256x128>(p.stages, piped, p.load_bytes);
+    return p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgMfma128>(p.stages, piped, p.load_bytes)
+                                        : gemm_kernel<CfgMfma64>(p.stages, piped, p.load_bytes);
 }
 
 int launch(const void *fn, int blocks, void *arg, hipStream_t stream, int threads = kThreads) {
@@ -259,17 +278,7 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     g.gm = (int)((M + p.bm - 1) / p.bm);
     g.gn = (int)((N + p.bn - 1) / p.bn);
     g.vec_store = aligned16(C) && ldc % 4 == 0;
-    const bool piped = fill_mode == MGEMM_FILL_PIPED;
-    const void *fn;
-    if (compute == MGEMM_COMPUTE_VALU)
-        fn = p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgValu128>(stages, piped, p.load_bytes)
-                                          : gemm_kernel<CfgValu64>(stages, piped, p.load_bytes);
-    else if (p.tile == MGEMM_TILE_256x128)
-        fn = gemm_kernel<CfgMfma256x128>(stages, piped, p.load_bytes);
-    else
-        fn = p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgMfma128>(stages, piped, p.load_bytes)
-                                          : gemm_kernel<CfgMfma64>(stages, piped, p.load_bytes);
-    return launch(fn, p.blocks, &g, s);
+    return launch(select_gemm(p), p.blocks, &g, s);
 }
 
 int mgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
@@ -280,7 +289,7 @@ int mgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
 
 int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, float *dst, int64_t ldd, int stages,
                     void *stream) {
-    if (stages < 1 || stages > 3)
+    if (stages < 1 || stages > kMaxPipedStages)
         return MGEMM_ERR_ARG;
     int st;
     if ((st = check_matrix(src, rows, cols, lds)) != MGEMM_OK || (st = check_matrix(dst, rows, cols, ldd)) != MGEMM_OK)
@@ -308,7 +317,7 @@ int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, f
     a.ntiles = (int)ntiles;
     const void *fn = copy_kernel(stages, W, vst);
     // persistent grid: as many blocks as fit on the device at once
-    static std::atomic<int> occ_cache[3][2][2];
+    static std::atomic<int> occ_cache[kMaxPipedStages][2][2];
     std::atomic<int> &oc = occ_cache[stages - 1][W == 16][vst];
     int occ = oc.load(std::memory_order_relaxed);
     if (occ == 0) {
@@ -322,17 +331,40 @@ int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, f
     return launch(fn, blocks, &a, s, kCopyThreads);
 }
 
+int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+                        const float *C, int64_t ldc, int stages, int fill_mode, int compute, int tile, int loader,
+                        int *blocks_per_cu) {
+    mgemm_plan_t p;
+    int st = plan_gemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader, &p);
+    if (st != MGEMM_OK)
+        return st;
+    if (blocks_per_cu == nullptr)
+        return MGEMM_ERR_ARG;
+    int dev;
+    if ((st = current_device(&dev)) != MGEMM_OK)
+        return st;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, select_gemm(p), kThreads, 0) != hipSuccess)
+        return MGEMM_ERR_LAUNCH;
+    *blocks_per_cu = occ;
+    return MGEMM_OK;
+}
+
 int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *events, int cap) {
-    if (stages < 1 || stages > 3 || slices < 0 || cap < 0 || (cap > 0 && events == nullptr) ||
-        (kind != 0 && kind != 1) || (fill_mode != MGEMM_FILL_SYNC && fill_mode != MGEMM_FILL_PIPED) ||
-        (kind == 1 && fill_mode != MGEMM_FILL_PIPED))
+    if (stages < 1 || slices < 0 || cap < 0 || (cap > 0 && events == nullptr) || (kind != 0 && kind != 1) ||
+        (fill_mode != MGEMM_FILL_SYNC && fill_mode != MGEMM_FILL_PIPED) ||
+        (kind == 1 && fill_mode != MGEMM_FILL_PIPED) ||
+        stages > (fill_mode == MGEMM_FILL_PIPED ? kMaxPipedStages : kMaxSyncStages))
         return MGEMM_ERR_ARG;
     Recorder r{events, cap, 0};
     if (fill_mode == MGEMM_FILL_PIPED) {
         switch (stages) {
         case 1: piped_schedule<1>(slices, r); break;
         case 2: piped_schedule<2>(slices, r); break;
-        default: piped_schedule<3>(slices, r); break;
+        case 3: piped_schedule<3>(slices, r); break;
+        case 4: piped_schedule<4>(slices, r); break;
+        case 5: piped_schedule<5>(slices, r); break;
+        default: piped_schedule<6>(slices, r); break;
         }
     } else {
         switch (stages) {

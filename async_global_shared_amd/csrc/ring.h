@@ -25,6 +25,9 @@
 
 namespace mgemm {
 
+constexpr int kMaxPipedStages = 6; // asynchronous ring depth
+constexpr int kMaxSyncStages = 3;  // register-staged ring depth (S-1 register sets)
+
 template <int I>
 struct Int {
     static constexpr int value = I;
@@ -44,12 +47,14 @@ MG_HD inline void static_for(F &&f) {
 //   barrier()            block barrier after the wave's LDS reads completed
 //   compute(slice, slot) consume `slot`, which holds `slice`
 // S == 1 has no lookahead (fetch, wait, compute, release). For S >= 2 the
-// prologue issues S-1 slices; iteration t waits for slice t, barriers (slice
-// t visible to all waves; slot (t-1) % S released by all waves), refills that
-// released slot with slice t+S-1, then computes slice t.
+// prologue issues S-1 slices; iteration t waits for slice t (leaving the
+// slices issued after it in flight: S-2 in the steady state, fewer in the
+// last S-2 iterations), barriers (slice t visible to all waves; slot
+// (t-1) % S released by all waves), refills that released slot with slice
+// t+S-1, then computes slice t.
 template <int S, class Ops>
 MG_HD inline void piped_schedule(int T, Ops &ops) {
-    static_assert(S >= 1 && S <= 3, "stages must be 1, 2 or 3");
+    static_assert(S >= 1 && S <= kMaxPipedStages, "stages must be 1 .. 6");
     if constexpr (S == 1) {
         for (int t = 0; t < T; ++t) {
             ops.issue(t, 0);
@@ -62,10 +67,12 @@ MG_HD inline void piped_schedule(int T, Ops &ops) {
         for (int s = 0; s < S - 1 && s < T; ++s)
             ops.issue(s, s);
         for (int t = 0; t < T; ++t) {
-            if (t + S - 2 < T)
-                ops.template wait<S - 2>();
-            else
-                ops.template wait<0>();
+            // slices issued after slice t so far: t+1 .. min(t+S-2, T-1)
+            const int pending = (t + S - 2 < T ? t + S - 2 : T - 1) - t;
+            static_for<0, S - 1>([&](auto p) {
+                if (pending == p.value)
+                    ops.template wait<p.value>();
+            });
             ops.barrier();
             if (t + S - 1 < T)
                 ops.issue(t + S - 1, (t + S - 1) % S);
@@ -86,7 +93,7 @@ MG_HD inline void piped_schedule(int T, Ops &ops) {
 // compile-time constants (the loop is unrolled by S-1).
 template <int S, class Ops>
 MG_HD inline void sync_schedule(int T, Ops &ops) {
-    static_assert(S >= 1 && S <= 3, "stages must be 1, 2 or 3");
+    static_assert(S >= 1 && S <= kMaxSyncStages, "stages must be 1, 2 or 3");
     if constexpr (S == 1) {
         for (int t = 0; t < T; ++t) {
             ops.template load<0>(t);

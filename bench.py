@@ -273,6 +273,7 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
         if n != big:
             del A, B, C
     res["gemm"] = gemm
+    res["stage_study"] = stage_study(m, torch, Ad8, Bd8, Cd8)
     # tile copy: 1 GiB fp32 ~ N(0,1), 64x64 tiles, 2 x bytes moved
     n_el = 1 << 28
     src = datagen.normal01_torch(datagen.SEED_COPY, n_el, device="cuda")
@@ -294,6 +295,35 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
     res["tile_copy_1GiB"] = copy
     del src, dst
     return res
+
+
+def stage_study(m, torch, Ad8, Bd8, Cd8):
+    """The lesson's exercise (ring depth swept, ratio to the synchronous fill,
+    LDS per block and what it costs in resident blocks), for its own 64x64x16
+    4x4 VALU kernel at N = 2048 and for the MFMA kernel at the full size."""
+    out = {}
+    for name, n, compute, tile in (("valu64_N2048", 2048, "valu", "64x64"),
+                                   (f"mfma128_N{Ad8.shape[0]}", Ad8.shape[0], "mfma", "128x128")):
+        if n == Ad8.shape[0]:
+            A, B, C = Ad8, Bd8, Cd8
+        else:
+            A, B = Ad8[:n, :n].contiguous(), Bd8[:n, :n].contiguous()
+            C = torch.empty((n, n), device="cuda")
+        flop = 2.0 * n ** 3
+        rows = {}
+        base = timed_launches(lambda: m.sgemm(A, B, C, stages=1, fill="sync", compute=compute, tile=tile),
+                              repeats=3)["ms_median"]
+        rows["sync_S1"] = {"ms": round(base, 4), "gflops": round(flop / base / 1e6, 1)}
+        for S in range(1, 7):
+            ms = timed_launches(lambda: m.sgemm(A, B, C, stages=S, fill="piped", compute=compute, tile=tile),
+                                repeats=3)["ms_median"]
+            p = m.plan(n, n, n, stages=S, fill="piped", compute=compute, tile=tile)
+            rows[f"piped_S{S}"] = {"ms": round(ms, 4), "gflops": round(flop / ms / 1e6, 1),
+                                   "piped_over_sync": round(ms / base, 3), "lds_bytes": p["lds_bytes"],
+                                   "blocks_per_cu": m.blocks_per_cu(n, n, n, stages=S, fill="piped",
+                                                                    compute=compute, tile=tile)}
+        out[name] = rows
+    return out
 
 
 def cpu_baseline(Ad, Bd, budget_s=12.0):

@@ -72,8 +72,10 @@ extern "C" {
 
 /*
  * C[0:M, 0:N] = A[0:M, 0:K] * B[0:K, 0:N]  (fp32, "Two kernels, one arithmetic").
- * stages in {1, 2, 3}: LDS ring depth; piped keeps stages-1 slices in flight
- * during compute (stages == 1: fetch, wait, compute, no overlap). fill_mode is
+ * stages: LDS ring depth, 1 .. 6 for MGEMM_FILL_PIPED (the pages' exercise
+ * sweeps the depth; 1 = fetch, wait, compute, no overlap) and 1 .. 3 for
+ * MGEMM_FILL_SYNC (stages-1 register sets); piped keeps stages-1 slices in
+ * flight during compute. fill_mode is
  * MGEMM_FILL_SYNC or MGEMM_FILL_PIPED. Uses the VALU compute tile and the
  * automatic tile and loader choice. For a fixed (shape, compute, tile), every
  * (stages, fill_mode, loader) gives bit-identical C. M == 0 or N == 0: no-op.
@@ -97,7 +99,7 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K,
 /*
  * dst[0:rows, 0:cols] = src[0:rows, 0:cols], streamed global -> LDS -> global
  * in 64 x 64 tiles through a `stages`-slot LDS ring filled asynchronously
- * (stages in {1, 2, 3}; 1 = no overlap). The bytes of dst equal those of src;
+ * (stages 1 .. 6; 1 = no overlap). The bytes of dst equal those of src;
  * padding columns of dst are not written. Isolates the fill bandwidth of the
  * GEMM's loader ("cp.async", section "Example: four 16-byte copies per
  * thread", which copies global -> shared -> global and checks equality).
@@ -137,6 +139,21 @@ int mgemm_plan_sgemm(int64_t M, int64_t N, int64_t K,
                      const float *C, int64_t ldc,
                      int stages, int fill_mode, int compute, int tile, int loader,
                      mgemm_plan_t *plan);
+
+/*
+ * Resident blocks per compute unit of the kernel mgemm_sgemm_ex would launch
+ * for these arguments (registers, LDS and wave limits together), for the
+ * stage-depth study of "Day 74 -- Async copies and pipelines" (section
+ * "Exercise": a deeper ring costs LDS per block and so resident blocks).
+ * Validates like mgemm_plan_sgemm, then queries the current device:
+ * MGEMM_ERR_ARCH without a gfx950 device.
+ */
+int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K,
+                        const float *A, int64_t lda,
+                        const float *B, int64_t ldb,
+                        const float *C, int64_t ldc,
+                        int stages, int fill_mode, int compute, int tile, int loader,
+                        int *blocks_per_cu);
 
 /*
  * Record the stage schedule that a kernel's ring executes for `slices` K

@@ -41,7 +41,8 @@ def sg(M=64, N=64, K=64, A=A0, lda=None, B=B0, ldb=None, C=C0, ldc=None, stages=
 
 @pytest.mark.parametrize("kw,want", [
     (dict(M=-1), m.ERR_ARG), (dict(N=-1), m.ERR_ARG), (dict(K=-1), m.ERR_ARG),
-    (dict(stages=0), m.ERR_ARG), (dict(stages=4), m.ERR_ARG), (dict(fill=2), m.ERR_ARG),
+    (dict(stages=0), m.ERR_ARG), (dict(stages=7), m.ERR_ARG), (dict(stages=4, fill=0), m.ERR_ARG),
+    (dict(fill=2), m.ERR_ARG),
     (dict(compute=2), m.ERR_ARG), (dict(tile=4), m.ERR_ARG), (dict(tile=3, compute=0), m.ERR_ARG), (dict(loader=3), m.ERR_ARG),
     (dict(lda=63), m.ERR_ARG), (dict(ldb=10), m.ERR_ARG), (dict(ldc=63), m.ERR_ARG),
     (dict(A=0), m.ERR_ARG), (dict(B=0), m.ERR_ARG), (dict(C=0), m.ERR_ARG),
@@ -62,6 +63,7 @@ def test_empty_operands_need_no_pointers():
 def test_copy_validation():
     f = m.mgemm_tile_copy
     assert f(10, 10, A0, 10, B0, 10, 0, None) == m.ERR_ARG
+    assert f(10, 10, A0, 10, B0, 10, 7, None) == m.ERR_ARG
     assert f(10, 10, A0, 9, B0, 10, 2, None) == m.ERR_ARG
     assert f(10, 10, A0, 10, A0 + 40, 10, 2, None) == m.ERR_ALIAS
     assert f(10, 10, 0, 10, B0, 10, 2, None) == m.ERR_ARG
@@ -84,10 +86,14 @@ def test_plan_tiles_loaders_and_lds():
     # misaligned base
     st, pl = m.mgemm_plan_sgemm(64, 64, 64, A0 + 4, 64, B0, 64, C0, 64, 2, 1, 0, 0, 0)
     assert st == m.OK and pl.load_bytes == 4
-    for S in (1, 2, 3):
+    for S in range(1, 7):
         for b in ("64x64", "128x128"):
             for ld in ("b128", "b32"):
-                assert m.plan(512, 512, 512, stages=S, tile=b, loader=ld)["max_vmcnt"] <= 63
+                p = m.plan(512, 512, 512, stages=S, tile=b, loader=ld)
+                assert p["max_vmcnt"] == min(63, max(0, S - 2) * p["loads_per_slice"])
+    # deep rings fit the 160 KiB of LDS: 6 stages of 256x128x16 fp32 tiles
+    p = m.plan(8192, 8192, 8192, stages=6, compute="mfma", tile="256x128")
+    assert p["lds_bytes"] == 6 * (256 + 128) * 16 * 4 <= 160 * 1024
 
 
 def test_lds_per_stage_matches_the_pages_budget():
@@ -193,22 +199,26 @@ def simulate_sync(events, S, T):
     assert loaded == list(range(T)) and computed == list(range(T))
 
 
-@pytest.mark.parametrize("S", [1, 2, 3])
-@pytest.mark.parametrize("fill", [0, 1])
+@pytest.mark.parametrize("S,fill", [(S, 1) for S in range(1, 7)] + [(S, 0) for S in (1, 2, 3)])
 def test_ring_schedule(S, fill):
-    for T in list(range(0, 12)) + [31, 40, 97]:
+    for T in list(range(0, 14)) + [31, 40, 97]:
         ev = m.mgemm_ring_trace(0, S, fill, T)
         if fill == 1:
             simulate_piped(ev, S, T)
             waits = [a for op, a, b in ev if op == 2]
             assert all(0 <= w <= max(S - 2, 0) for w in waits)
+            # the waits are exact: each leaves in flight exactly the slices issued after the awaited one
+            if S >= 2:
+                assert waits == [min(T - 1, t + S - 2) - t for t in range(T)]
         else:
             simulate_sync(ev, S, T)
-    assert m.mgemm_ring_trace(1, S, 1, 5) == m.mgemm_ring_trace(0, S, 1, 5)
+    if fill == 1:
+        assert m.mgemm_ring_trace(1, S, 1, 5) == m.mgemm_ring_trace(0, S, 1, 5)
 
 
 def test_ring_trace_rejects_bad_arguments():
-    assert m.lib().mgemm_ring_trace(0, 4, 1, 3, None, 0) == m.ERR_ARG
+    assert m.lib().mgemm_ring_trace(0, 7, 1, 3, None, 0) == m.ERR_ARG
+    assert m.lib().mgemm_ring_trace(0, 4, 0, 3, None, 0) == m.ERR_ARG
     assert m.lib().mgemm_ring_trace(1, 2, 0, 3, None, 0) == m.ERR_ARG
     assert m.lib().mgemm_ring_trace(2, 2, 1, 3, None, 0) == m.ERR_ARG
 
@@ -268,50 +278,123 @@ def isa():
     return _kernels(open(m.ISA_PATH).read())
 
 
-@pytest.mark.parametrize("cfg", ["CfgValu64", "CfgValu128", "CfgMfma64", "CfgMfma128"])
+CFGS = ["CfgValu64", "CfgValu128", "CfgMfma64", "CfgMfma128", "CfgMfma256x128"]
+
+
+@pytest.mark.parametrize("cfg", CFGS)
 def test_isa_fill_instructions(isa, cfg):
     """Piped kernels fill LDS with buffer_load ... lds and no ds_write; sync
     kernels fill through VGPRs (ds_write) and have no LDS-direct load."""
-    for S in (1, 2, 3):
+    for S in range(1, 7):
         for W in (16, 4):
             body = "\n".join(isa[_name(cfg, S, True, W)])
             width = "dwordx4" if W == 16 else "dword"
             assert re.search(rf"buffer_load_{width} .* lds", body), (cfg, S, W)
             assert "ds_write" not in body, (cfg, S, W)
+            assert "v_pk_fma_f32" not in body
+            if S > 3:
+                assert _name(cfg, S, False, W) not in isa  # no register-staged ring that deep
+                continue
             sbody = "\n".join(isa[_name(cfg, S, False, W)])
             assert " lds" not in sbody.replace("lds_", "") or not re.search(r"buffer_load\S* .* lds", sbody)
             assert "ds_write" in sbody
             assert "v_pk_fma_f32" not in body and "v_pk_fma_f32" not in sbody
 
 
-@pytest.mark.parametrize("cfg", ["CfgValu64", "CfgValu128", "CfgMfma64", "CfgMfma128"])
+def _cfg(lines):
+    """Basic blocks of one kernel's assembly: list of (label, instructions,
+    successor labels), following labels and s_branch / s_cbranch_*."""
+    blocks, cur, body = [], "entry", []
+    def close(nxt):
+        blocks.append([cur, body, nxt])
+    for raw in lines:
+        l = raw.split(";")[0].rstrip()
+        if not l.strip() or l.strip().startswith("."):
+            mm = re.match(r"^(\.LBB\w+):", raw)
+            if mm:
+                close(None)
+                cur, body = mm.group(1), []
+            continue
+        ins = l.strip()
+        body.append(ins)
+        op = ins.split()[0]
+        if op == "s_branch" or op.startswith("s_cbranch") or op in ("s_endpgm", "s_setpc_b64"):
+            blocks.append([cur, body, ins])
+            cur, body = cur + "+", []
+    blocks.append([cur, body, None])
+    out = []
+    for i, (lab, ins, term) in enumerate(blocks):
+        succ = []
+        op = term.split()[0] if isinstance(term, str) else None
+        if op and (op == "s_branch" or op.startswith("s_cbranch")):
+            succ.append(term.split()[1])
+        if op not in ("s_branch", "s_endpgm", "s_setpc_b64") and i + 1 < len(blocks):
+            succ.append(blocks[i + 1][0])
+        out.append((lab, ins, succ))
+    return out
+
+
+def _drain_before_compute(lines, op):
+    """True if some path from a ring barrier reaches the compute instruction
+    `op` through an s_waitcnt vmcnt(0)."""
+    blocks = _cfg(lines)
+    index = {lab: i for i, (lab, _, _) in enumerate(blocks)}
+    # states: (block index, position, drained?)
+    starts = [(i, k + 1) for i, (_, ins, _) in enumerate(blocks) for k, x in enumerate(ins) if x == "s_barrier"]
+    seen, stack = set(), [(i, k, False) for i, k in starts]
+    found_compute = False
+    while stack:
+        i, k, drained = stack.pop()
+        if (i, k, drained) in seen:
+            continue
+        seen.add((i, k, drained))
+        lab, ins, succ = blocks[i]
+        stop = False
+        for x in ins[k:]:
+            if x == "s_barrier":
+                stop = True
+                break
+            if "vmcnt(0)" in x:
+                drained = True
+            if x.startswith(op):
+                found_compute = True
+                if drained:
+                    return True, True
+                stop = True
+                break
+        if not stop:
+            for sname in succ:
+                if sname in index:
+                    stack.append((index[sname], 0, drained))
+    return False, found_compute
+
+
+@pytest.mark.parametrize("cfg", CFGS)
 def test_isa_compute_does_not_drain_the_prefetch(isa, cfg):
-    """In the piped S >= 2 kernels no s_waitcnt vmcnt(0) sits between a ring
-    barrier and the arithmetic that follows it: the compute runs while the
-    next slices are still in flight."""
-    op = "v_mfma_f32_32x32x2_f32" if "Mfma" in cfg else "v_fma"
-    for S in (2, 3):
+    """In the piped S >= 2 kernels no path through the control-flow graph goes
+    from a ring barrier through s_waitcnt vmcnt(0) to the arithmetic: the
+    compute runs while the next slices are still in flight."""
+    op = "v_mfma_f32_32x32x2_f32" if "Mfma" in cfg else "v_fmac_f32"
+    for S in range(2, 7):
         for W in (16, 4):
             lines = isa[_name(cfg, S, True, W)]
-            segs, cur = [], []
-            for l in lines:
-                if "s_barrier" in l:
-                    segs.append(cur)
-                    cur = []
-                else:
-                    cur.append(l)
-            segs.append(cur)
-            compute_segs = [s for s in segs[1:] if any(op in l for l in s)]
-            assert compute_segs, (cfg, S, W)
-            for s in compute_segs:
-                head = []
-                for l in s:
-                    if op in l:
-                        break
-                    head.append(l)
-                assert not any("vmcnt(0)" in l for l in head), (cfg, S, W)
-            if S == 3:
+            drained, reached = _drain_before_compute(lines, op)
+            assert reached, (cfg, S, W)
+            assert not drained, (cfg, S, W)
+            if S >= 3:
                 body = "\n".join(lines)
-                n = m.plan(1024, 1024, 1024, stages=3, tile="128x128" if "128" in cfg else "64x64",
+                tile = {"CfgMfma256x128": "256x128"}.get(cfg, "128x128" if "128" in cfg else "64x64")
+                n = m.plan(1024, 1024, 1024, stages=S, tile=tile, compute="mfma" if "Mfma" in cfg else "valu",
                            loader="b128" if W == 16 else "b32")["max_vmcnt"]
-                assert f"s_waitcnt vmcnt({n})" in body, (cfg, W, n)
+                assert f"s_waitcnt vmcnt({n})" in body, (cfg, S, W, n)
+
+
+def test_isa_drain_checker_sees_a_drain():
+    """The path checker flags a vmcnt(0) between barrier and compute."""
+    lines = ["s_barrier", ".LBB0_1:", "s_waitcnt vmcnt(0)", "v_fmac_f32_e32 v1, v2, v3", "s_endpgm"]
+    assert _drain_before_compute(lines, "v_fmac_f32") == (True, True)
+    lines = ["s_waitcnt vmcnt(0)", "s_barrier", "s_cbranch_scc1 .LBB0_2", "s_waitcnt vmcnt(0)", ".LBB0_2:",
+             "v_fmac_f32_e32 v1, v2, v3", "s_endpgm"]
+    assert _drain_before_compute(lines, "v_fmac_f32") == (True, True)
+    lines = ["s_waitcnt vmcnt(0)", "s_barrier", "s_waitcnt lgkmcnt(0)", "v_fmac_f32_e32 v1, v2, v3"]
+    assert _drain_before_compute(lines, "v_fmac_f32") == (False, True)

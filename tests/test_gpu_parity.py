@@ -93,6 +93,46 @@ def test_every_variant_ragged(layout):
                         assert same_bits(C, ref), f"{layout} {compute} {tile} {fill} S={S} {ld} != first variant"
 
 
+@pytest.mark.parametrize("layout", ["padded_ld", "misaligned"])
+def test_deep_piped_rings(layout):
+    """Rings of 4-6 stages (the lesson's exercise sweeps the depth) give the
+    same bits as the synchronous fill, for every compute tile and loader."""
+    M, N, K, lda, ldb, ldc, (oa, ob, oc) = LAYOUTS[layout]
+    K = 517  # 33 slices: the tail of every deep ring is exercised
+    A, B = _inputs("uniform", M, N, K, seed=70)
+    Ad = padded_device(A, K + 3, offset=oa)
+    Bd = padded_device(B, ldb, offset=ob)
+    for compute, tile in TILES:
+        ref = full_rows(run(Ad, Bd, out_device(M, N, ldc, offset=oc), compute=compute, tile=tile, fill="sync",
+                            stages=1))
+        check_bound(ref[:, :N], A, B, what=f"{layout} {compute} {tile} sync S=1")
+        for S in (4, 5, 6):
+            for ld in ("auto", "b32"):
+                C = full_rows(run(Ad, Bd, out_device(M, N, ldc, offset=oc), compute=compute, tile=tile,
+                                  fill="piped", stages=S, loader=ld))
+                assert same_bits(C, ref), (layout, compute, tile, S, ld)
+
+
+def test_deep_ring_copy():
+    x = datagen.matrix("normal", datagen.SEED_COPY, 700, 900)
+    src = padded_device(x, 904)
+    for S in (4, 5, 6):
+        dst = out_device(700, 900, 905)
+        m.tile_copy(src, dst, stages=S)
+        torch.cuda.synchronize()
+        full = full_rows(dst)
+        assert same_bits(np.ascontiguousarray(full[:, :900]), x) and np.all(full[:, 900:] == SENTINEL), S
+
+
+def test_blocks_per_cu_query():
+    """Deeper rings hold more LDS per block; the query reports what fits."""
+    occ = [m.blocks_per_cu(8192, 8192, 8192, stages=S, compute="mfma", tile="128x128") for S in range(1, 7)]
+    assert all(1 <= o <= 8 for o in occ)
+    assert occ == sorted(occ, reverse=True)  # never more resident blocks with a deeper ring
+    with pytest.raises(m.MgemmError):
+        m.blocks_per_cu(64, 64, 64, stages=4, fill="sync")
+
+
 def test_b128_and_b32_loaders_agree_when_both_apply():
     M, N, K = 384, 256, 320
     A, B = _inputs("uniform", M, N, K, seed=20)
