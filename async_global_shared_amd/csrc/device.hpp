@@ -143,6 +143,13 @@ struct ValuTile {
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = 0.0f;
     }
+    __device__ void poison() {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_nanf("");
+    }
     __device__ int row(int h, int i) const { return 64 * h + 4 * tr + i; }
     __device__ int col(int h) const { return 64 * h + 4 * tc; }
 
@@ -223,6 +230,16 @@ struct MfmaTile {
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     acc[a][b][i] = 0.0f;
+    }
+
+    __device__ void poison() {
+#pragma unroll
+        for (int a = 0; a < WTM; ++a)
+#pragma unroll
+            for (int b = 0; b < WTN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[a][b][i] = __builtin_nanf("");
     }
 
     __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
@@ -470,6 +487,132 @@ __global__ void __launch_bounds__(kThreads) sgemm_kernel(GemmArgs g) {
         piped_schedule<S>(T, ops);
     else
         sync_schedule<S>(T, ops);
+    ops.tile.store(g.C, g.ldc, m0, n0, g.M, g.N, g.vec_store != 0);
+}
+
+// ---- warp-specialised ring ------------------------------------------------------
+//
+// The producer/consumer form of the pipeline ("A study on CUDA async memcpy",
+// sections "block-scoped pipeline" and the warp-specialisation remark after
+// the real-world example): some waves only fill, the others only compute, and
+// a pair of per-stage events, "produced" and "consumed", replaces the block
+// barrier. gfx950 has no mbarrier, so each event is a cumulative LDS counter:
+//   ready[slot]    += 1 by each filling wave once its own fills of the slice
+//                  in that slot have landed (its vmcnt counts nothing else);
+//   consumed[slot] += 1 by each computing wave once its LDS reads of that
+//                  slice have completed (lgkmcnt(0)).
+// Slice t uses slot t % S for the (t / S)-th time, so it is ready when
+// ready[slot] >= kWsFill * (t / S + 1), and its slot may be refilled with slice
+// t + S once consumed[slot] >= kWsCompute * (t / S + 1). Waves of one block are
+// co-resident, so every wait is eventually satisfied; a bounded spin still
+// guards each wait: on timeout the block marks itself broken, every wave
+// leaves its loop and the computing waves write NaN, so a protocol error
+// shows up as a wrong result rather than a hang.
+constexpr int kWsCompute = 4;          // computing waves (the 2 x 2 compute tile)
+constexpr int kWsFill = 4;             // filling waves (same unit split as the 4-wave ring)
+constexpr int kWsThreads = 64 * (kWsCompute + kWsFill);
+constexpr unsigned kWsSpinLimit = 1u << 22;
+
+struct WsCounters {
+    int ready[kMaxPipedStages];
+    int consumed[kMaxPipedStages];
+    int broken;
+};
+
+__device__ inline int lds_load_relaxed(int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Spin until *p >= target. Returns false when the block is (or becomes) broken.
+__device__ inline bool ws_wait_ge(int *p, int target, int *broken) {
+    for (unsigned i = 0; i < kWsSpinLimit; ++i) {
+        if (lds_load_relaxed(p) >= target) {
+            asm volatile("" ::: "memory"); // later LDS reads stay after the observed event
+            return true;
+        }
+        if (lds_load_relaxed(broken))
+            return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __hip_atomic_store(broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return false;
+}
+
+__device__ inline void ws_arrive(int *p, int lane) {
+    if (lane == 0)
+        __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <class Cfg, int S, int W>
+__global__ void __launch_bounds__(kWsThreads) sgemm_ws_kernel(GemmArgs g) {
+    using Tile = typename Cfg::Tile;
+    using Ops = PipedOps<Tile, W>;
+    static_assert(S >= 1 && S <= kMaxPipedStages, "stages");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S * Ops::SLOT];
+    __shared__ WsCounters ctr;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid < 2 * kMaxPipedStages + 1)
+        ((int *)&ctr)[tid] = 0;
+    __syncthreads();
+
+    int tm, tn;
+    block_tile(blockIdx.x, g.gm, g.gn, tm, tn);
+    const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+    const int T = (g.K + kBK - 1) / kBK;
+
+    Ops ops;
+    ops.smem = smem;
+    ops.lane = lane;
+    ops.Ablk = g.A + (size_t)m0 * g.lda;
+    ops.Bblk = g.B + n0;
+    ops.ldb = g.ldb;
+    ops.K = g.K;
+    ops.a_rows = g.M - m0;
+    ops.b_cols = g.N - n0;
+
+    if (wave >= kWsCompute) {
+        // filling wave f: the fills of unit split f of every slice
+        ops.wave = wave - kWsCompute;
+        ops.oa.init(lane, ops.wave, g.lda);
+        ops.ob.init(lane, ops.wave, g.ldb);
+        constexpr int L = Ops::OA::U + Ops::OB::U; // fill instructions per slice
+        constexpr int D = S >= 2 ? S - 2 : 0;      // slices left in flight when one is signalled
+        int signalled = 0;
+        for (int t = 0; t < T; ++t) {
+            const int slot = t % S;
+            if (t >= S && !ws_wait_ge(&ctr.consumed[slot], kWsCompute * (t / S), &ctr.broken)) {
+                wait_vm<0>(); // no fill of this wave outlives it
+                return;
+            }
+            ops.issue(t, slot);
+            if (t >= D) {
+                wait_vm<D * L>();
+                ws_arrive(&ctr.ready[signalled % S], lane);
+                ++signalled;
+            }
+        }
+        wait_vm<0>();
+        for (; signalled < T; ++signalled)
+            ws_arrive(&ctr.ready[signalled % S], lane);
+        return;
+    }
+
+    // computing waves 0..3: the same compute tile as the barrier ring
+    ops.tile.init(tid);
+    bool ok = true;
+    for (int t = 0; t < T && ok; ++t) {
+        const int slot = t % S;
+        ok = ws_wait_ge(&ctr.ready[slot], kWsFill * (t / S + 1), &ctr.broken);
+        if (ok) {
+            ops.compute(t, slot);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); // this wave's reads of the slot are done
+            ws_arrive(&ctr.consumed[slot], lane);
+        }
+    }
+    if (!ok)
+        ops.tile.poison();
     ops.tile.store(g.C, g.ldc, m0, n0, g.M, g.N, g.vec_store != 0);
 }
 

@@ -58,7 +58,8 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
               mgemm_plan_t *pl) {
     if (M < 0 || N < 0 || K < 0)
         return MGEMM_ERR_ARG;
-    if (stages < 1 || stages > kMaxPipedStages || (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED) ||
+    if (stages < 1 || stages > kMaxPipedStages ||
+        (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED && fill != MGEMM_FILL_PIPED_WS) ||
         (fill == MGEMM_FILL_SYNC && stages > kMaxSyncStages) ||
         (compute != MGEMM_COMPUTE_VALU && compute != MGEMM_COMPUTE_MFMA) || tile < MGEMM_TILE_AUTO ||
         tile > MGEMM_TILE_256x128 || loader < MGEMM_LOADER_AUTO || loader > MGEMM_LOADER_B32 ||
@@ -101,17 +102,17 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
     p.bm = bm;
     p.bn = bn;
     p.bk = kBK;
-    p.threads = kThreads;
+    p.threads = fill == MGEMM_FILL_PIPED_WS ? kWsThreads : kThreads;
     p.blocks = (int)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
     p.load_bytes = W;
     p.slices = (int)((K + kBK - 1) / kBK);
     p.stages = stages;
     p.fill_mode = fill;
-    p.lds_bytes = stages * (bm * kBK + kBK * bn) * 4;
+    p.lds_bytes = stages * (bm * kBK + kBK * bn) * 4 + (fill == MGEMM_FILL_PIPED_WS ? (int)sizeof(WsCounters) : 0);
     // one 64-lane instruction moves 64*W bytes; a slice of both operands is
     // (bm+bn)*16*4 bytes, shared by the 4 waves
     p.loads_per_slice = ((bm + bn) * kBK * 4) / (64 * W) / kWaves;
-    p.max_vmcnt = fill == MGEMM_FILL_PIPED ? std::min(63, std::max(0, stages - 2) * p.loads_per_slice) : 0;
+    p.max_vmcnt = fill != MGEMM_FILL_SYNC ? std::min(63, std::max(0, stages - 2) * p.loads_per_slice) : 0;
     if (pl)
         *pl = p;
     return MGEMM_OK;
@@ -139,27 +140,64 @@ int current_device(int *dev) {
 
 // ---- kernel tables ----------------------------------------------------------------
 
+} // namespace
+
+// Every kernel is instantiated explicitly: referencing the templates only
+// through the dispatch functions below left some host-side launch stubs
+// undefined with this compiler.
+#define MG_GEMM_INST(CFG, S, W)                                                                          \
+    template __global__ void mgemm::sgemm_kernel<mgemm::CFG, S, true, W>(mgemm::GemmArgs);               \
+    template __global__ void mgemm::sgemm_ws_kernel<mgemm::CFG, S, W>(mgemm::GemmArgs);
+#define MG_GEMM_SYNC_INST(CFG, S, W)                                                                     \
+    template __global__ void mgemm::sgemm_kernel<mgemm::CFG, S, false, W>(mgemm::GemmArgs);
+#define MG_GEMM_CFG(CFG)                                                                                 \
+    MG_GEMM_INST(CFG, 1, 16) MG_GEMM_INST(CFG, 2, 16) MG_GEMM_INST(CFG, 3, 16) MG_GEMM_INST(CFG, 4, 16)  \
+    MG_GEMM_INST(CFG, 5, 16) MG_GEMM_INST(CFG, 6, 16) MG_GEMM_INST(CFG, 1, 4) MG_GEMM_INST(CFG, 2, 4)    \
+    MG_GEMM_INST(CFG, 3, 4) MG_GEMM_INST(CFG, 4, 4) MG_GEMM_INST(CFG, 5, 4) MG_GEMM_INST(CFG, 6, 4)      \
+    MG_GEMM_SYNC_INST(CFG, 1, 16) MG_GEMM_SYNC_INST(CFG, 2, 16) MG_GEMM_SYNC_INST(CFG, 3, 16)            \
+    MG_GEMM_SYNC_INST(CFG, 1, 4) MG_GEMM_SYNC_INST(CFG, 2, 4) MG_GEMM_SYNC_INST(CFG, 3, 4)
+MG_GEMM_CFG(CfgValu64)
+MG_GEMM_CFG(CfgValu128)
+MG_GEMM_CFG(CfgMfma64)
+MG_GEMM_CFG(CfgMfma128)
+MG_GEMM_CFG(CfgMfma256x128)
+#define MG_COPY_INST(S)                                                                                  \
+    template __global__ void mgemm::tile_copy_kernel<S, 16, true>(mgemm::CopyArgs);                      \
+    template __global__ void mgemm::tile_copy_kernel<S, 16, false>(mgemm::CopyArgs);                     \
+    template __global__ void mgemm::tile_copy_kernel<S, 4, true>(mgemm::CopyArgs);                       \
+    template __global__ void mgemm::tile_copy_kernel<S, 4, false>(mgemm::CopyArgs);
+MG_COPY_INST(1)
+MG_COPY_INST(2)
+MG_COPY_INST(3)
+MG_COPY_INST(4)
+MG_COPY_INST(5)
+MG_COPY_INST(6)
+
+namespace {
+
 template <class Cfg, int S, int W>
-const void *gk(bool piped) {
+const void *gk(int fill) {
     if constexpr (S <= kMaxSyncStages)
-        if (!piped)
+        if (fill == MGEMM_FILL_SYNC)
             return (const void *)&sgemm_kernel<Cfg, S, false, W>;
+    if (fill == MGEMM_FILL_PIPED_WS)
+        return (const void *)&sgemm_ws_kernel<Cfg, S, W>;
     return (const void *)&sgemm_kernel<Cfg, S, true, W>;
 }
 template <class Cfg, int W>
-const void *gemm_kernel_w(int S, bool piped) {
+const void *gemm_kernel_w(int S, int fill) {
     switch (S) {
-    case 1: return gk<Cfg, 1, W>(piped);
-    case 2: return gk<Cfg, 2, W>(piped);
-    case 3: return gk<Cfg, 3, W>(piped);
-    case 4: return gk<Cfg, 4, W>(piped);
-    case 5: return gk<Cfg, 5, W>(piped);
-    default: return gk<Cfg, 6, W>(piped);
+    case 1: return gk<Cfg, 1, W>(fill);
+    case 2: return gk<Cfg, 2, W>(fill);
+    case 3: return gk<Cfg, 3, W>(fill);
+    case 4: return gk<Cfg, 4, W>(fill);
+    case 5: return gk<Cfg, 5, W>(fill);
+    default: return gk<Cfg, 6, W>(fill);
     }
 }
 template <class Cfg>
-const void *gemm_kernel(int S, bool piped, int W) {
-    return W == 16 ? gemm_kernel_w<Cfg, 16>(S, piped) : gemm_kernel_w<Cfg, 4>(S, piped);
+const void *gemm_kernel(int S, int fill, int W) {
+    return W == 16 ? gemm_kernel_w<Cfg, 16>(S, fill) : gemm_kernel_w<Cfg, 4>(S, fill);
 }
 
 template <int S>
@@ -180,7 +218,7 @@ const void *copy_kernel(int S, int W, bool vst) {
 }
 
 const void *select_gemm(const mgemm_plan_t &p) {
-    const bool piped = p.fill_mode == MGEMM_FILL_PIPED;
+    const int piped = p.fill_mode;
     if (p.compute == MGEMM_COMPUTE_VALU)
         return p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgValu128>(p.stages, piped, p.load_bytes)
                                             : gemm_kernel<CfgValu64>(p.stages, piped, p.load_bytes);
@@ -278,7 +316,7 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     g.gm = (int)((M + p.bm - 1) / p.bm);
     g.gn = (int)((N + p.bn - 1) / p.bn);
     g.vec_store = aligned16(C) && ldc % 4 == 0;
-    return launch(select_gemm(p), p.blocks, &g, s);
+    return launch(select_gemm(p), p.blocks, &g, s, p.threads);
 }
 
 int mgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
@@ -344,7 +382,7 @@ int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K, const float *A, int64_t
     if ((st = current_device(&dev)) != MGEMM_OK)
         return st;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, select_gemm(p), kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, select_gemm(p), p.threads, 0) != hipSuccess)
         return MGEMM_ERR_LAUNCH;
     *blocks_per_cu = occ;
     return MGEMM_OK;

@@ -314,14 +314,15 @@ def stage_study(m, torch, Ad8, Bd8, Cd8):
         base = timed_launches(lambda: m.sgemm(A, B, C, stages=1, fill="sync", compute=compute, tile=tile),
                               repeats=3)["ms_median"]
         rows["sync_S1"] = {"ms": round(base, 4), "gflops": round(flop / base / 1e6, 1)}
-        for S in range(1, 7):
-            ms = timed_launches(lambda: m.sgemm(A, B, C, stages=S, fill="piped", compute=compute, tile=tile),
-                                repeats=3)["ms_median"]
-            p = m.plan(n, n, n, stages=S, fill="piped", compute=compute, tile=tile)
-            rows[f"piped_S{S}"] = {"ms": round(ms, 4), "gflops": round(flop / ms / 1e6, 1),
-                                   "piped_over_sync": round(ms / base, 3), "lds_bytes": p["lds_bytes"],
-                                   "blocks_per_cu": m.blocks_per_cu(n, n, n, stages=S, fill="piped",
-                                                                    compute=compute, tile=tile)}
+        for fill in ("piped", "piped_ws"):
+            for S in range(1, 7):
+                ms = timed_launches(lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute, tile=tile),
+                                    repeats=3)["ms_median"]
+                p = m.plan(n, n, n, stages=S, fill=fill, compute=compute, tile=tile)
+                rows[f"{fill}_S{S}"] = {"ms": round(ms, 4), "gflops": round(flop / ms / 1e6, 1),
+                                        "piped_over_sync": round(ms / base, 3), "lds_bytes": p["lds_bytes"],
+                                        "blocks_per_cu": m.blocks_per_cu(n, n, n, stages=S, fill=fill,
+                                                                         compute=compute, tile=tile)}
         out[name] = rows
     return out
 

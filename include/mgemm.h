@@ -46,6 +46,8 @@ extern "C" {
 /* fill_mode: how LDS tiles are filled ("Two kernels, one arithmetic"). */
 #define MGEMM_FILL_SYNC 0  /* global -> VGPR -> LDS; stages>=2 stage slices in registers */
 #define MGEMM_FILL_PIPED 1 /* asynchronous global -> LDS (buffer_load ... lds) ring */
+#define MGEMM_FILL_PIPED_WS 2 /* the same asynchronous fill issued by dedicated filling waves;
+                                 per-slot LDS counters replace the block barrier (512 threads) */
 
 /* compute: the inner product on the LDS tiles. */
 #define MGEMM_COMPUTE_VALU 0 /* per element fma chain, k ascending (the pages' computeTile) */
@@ -73,10 +75,11 @@ extern "C" {
 /*
  * C[0:M, 0:N] = A[0:M, 0:K] * B[0:K, 0:N]  (fp32, "Two kernels, one arithmetic").
  * stages: LDS ring depth, 1 .. 6 for MGEMM_FILL_PIPED (the pages' exercise
- * sweeps the depth; 1 = fetch, wait, compute, no overlap) and 1 .. 3 for
- * MGEMM_FILL_SYNC (stages-1 register sets); piped keeps stages-1 slices in
- * flight during compute. fill_mode is
- * MGEMM_FILL_SYNC or MGEMM_FILL_PIPED. Uses the VALU compute tile and the
+ * sweeps the depth; 1 = fetch, wait, compute, no overlap) and for
+ * MGEMM_FILL_PIPED_WS, 1 .. 3 for MGEMM_FILL_SYNC (stages-1 register sets);
+ * piped keeps stages-1 slices in flight during compute. fill_mode is
+ * MGEMM_FILL_SYNC, MGEMM_FILL_PIPED or MGEMM_FILL_PIPED_WS ("A study on CUDA
+ * async memcpy", producer/consumer pipeline). Uses the VALU compute tile and the
  * automatic tile and loader choice. For a fixed (shape, compute, tile), every
  * (stages, fill_mode, loader) gives bit-identical C. M == 0 or N == 0: no-op.
  * K == 0: C[0:M, 0:N] = +0. Cells of C outside M x N are never written.
@@ -164,7 +167,8 @@ int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K,
  * 4 = compute(slice a from slot b), 5 = store register set a -> slot b
  * (sync fill), 6 = load slice a into register set b (sync fill).
  * Returns the number of events (which may exceed cap; only cap are written),
- * or MGEMM_ERR_ARG. Host only; no device needed.
+ * or MGEMM_ERR_ARG (also for MGEMM_FILL_PIPED_WS, whose waves follow
+ * separate filling and computing loops). Host only; no device needed.
  */
 int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *events, int cap);
 

@@ -24,6 +24,14 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_no_undefined_kernel_symbols():
+    """Every kernel the dispatch tables name has its host launch stub."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", m.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    undefined = [l for l in out.splitlines() if " U _ZN5mgemm" in l]
+    assert not undefined, undefined[:5]
+
+
 def test_version_and_status_strings():
     assert m.mgemm_version() == m.MGEMM_VERSION
     for s in (m.OK, m.ERR_ARG, m.ERR_ALIAS, m.ERR_ARCH, m.ERR_LAUNCH, m.ERR_UNSUPPORTED):
@@ -42,7 +50,7 @@ def sg(M=64, N=64, K=64, A=A0, lda=None, B=B0, ldb=None, C=C0, ldc=None, stages=
 @pytest.mark.parametrize("kw,want", [
     (dict(M=-1), m.ERR_ARG), (dict(N=-1), m.ERR_ARG), (dict(K=-1), m.ERR_ARG),
     (dict(stages=0), m.ERR_ARG), (dict(stages=7), m.ERR_ARG), (dict(stages=4, fill=0), m.ERR_ARG),
-    (dict(fill=2), m.ERR_ARG),
+    (dict(fill=3), m.ERR_ARG),
     (dict(compute=2), m.ERR_ARG), (dict(tile=4), m.ERR_ARG), (dict(tile=3, compute=0), m.ERR_ARG), (dict(loader=3), m.ERR_ARG),
     (dict(lda=63), m.ERR_ARG), (dict(ldb=10), m.ERR_ARG), (dict(ldc=63), m.ERR_ARG),
     (dict(A=0), m.ERR_ARG), (dict(B=0), m.ERR_ARG), (dict(C=0), m.ERR_ARG),
@@ -94,6 +102,13 @@ def test_plan_tiles_loaders_and_lds():
     # deep rings fit the 160 KiB of LDS: 6 stages of 256x128x16 fp32 tiles
     p = m.plan(8192, 8192, 8192, stages=6, compute="mfma", tile="256x128")
     assert p["lds_bytes"] == 6 * (256 + 128) * 16 * 4 <= 160 * 1024
+
+
+def test_plan_warp_specialised():
+    p = m.plan(8192, 8192, 8192, stages=3, fill="piped_ws", compute="mfma")
+    assert p["threads"] == 512 and p["fill_mode"] == 2
+    assert p["lds_bytes"] == 3 * 16384 + 13 * 4 and p["max_vmcnt"] == 4
+    assert m.lib().mgemm_ring_trace(0, 2, 2, 3, None, 0) == m.ERR_ARG
 
 
 def test_lds_per_stage_matches_the_pages_budget():
@@ -398,3 +413,18 @@ def test_isa_drain_checker_sees_a_drain():
     assert _drain_before_compute(lines, "v_fmac_f32") == (True, True)
     lines = ["s_waitcnt vmcnt(0)", "s_barrier", "s_waitcnt lgkmcnt(0)", "v_fmac_f32_e32 v1, v2, v3"]
     assert _drain_before_compute(lines, "v_fmac_f32") == (False, True)
+
+
+@pytest.mark.parametrize("cfg", CFGS)
+def test_isa_warp_specialised(isa, cfg):
+    """The warp-specialised kernels synchronise through LDS counters: one
+    start-up barrier only, polls with s_sleep, ds_add arrivals, and the
+    asynchronous fill."""
+    for S in range(1, 7):
+        for W in (16, 4):
+            name = f"_ZN5mgemm15sgemm_ws_kernelINS_{len(cfg)}{cfg}ELi{S}ELi{W}EEEvNS_8GemmArgsE"
+            body = "\n".join(isa[name])
+            assert body.count("s_barrier") == 1, (cfg, S, W)
+            assert "ds_add_u32" in body and "s_sleep" in body
+            assert re.search(r"buffer_load_dword\S* .* lds", body)
+            assert "flat_atomic" not in body and "flat_load" not in body

@@ -45,7 +45,8 @@ def test_square_full_size(n):
         check_bound(C_rows, A_rows, B, what=f"{n}^3 {compute} piped S=3 (sampled rows)")
         other = torch.empty_like(ref)
         variants = [("sync", 1), ("piped", 2)] if compute == "valu" and n == 8192 else \
-            [("sync", 1), ("sync", 2), ("sync", 3), ("piped", 1), ("piped", 2), ("piped", 4), ("piped", 6)]
+            [("sync", 1), ("sync", 2), ("sync", 3), ("piped", 1), ("piped", 2), ("piped", 4), ("piped", 6),
+             ("piped_ws", 2), ("piped_ws", 3)]
         for fill, S in variants:
             other.fill_(float("nan"))
             m.sgemm(Ad, Bd, other, stages=S, fill=fill, compute=compute, tile="128x128")

@@ -113,6 +113,26 @@ def test_deep_piped_rings(layout):
                 assert same_bits(C, ref), (layout, compute, tile, S, ld)
 
 
+@pytest.mark.parametrize("layout", ["aligned", "misaligned", "tiny_k"])
+def test_warp_specialised_ring(layout):
+    """Dedicated filling waves with per-slot LDS counters give the same bits as
+    the synchronous fill, for every compute tile, depth and loader."""
+    M, N, K, lda, ldb, ldc, (oa, ob, oc) = LAYOUTS[layout]
+    A, B = _inputs("uniform", M, N, K, seed=80)
+    Ad = padded_device(A, lda, offset=oa)
+    Bd = padded_device(B, ldb, offset=ob)
+    for compute, tile in TILES:
+        ref = full_rows(run(Ad, Bd, out_device(M, N, ldc, offset=oc), compute=compute, tile=tile, fill="sync",
+                            stages=1))
+        check_bound(ref[:, :N], A, B, what=f"{layout} {compute} {tile} sync S=1")
+        for S in range(1, 7):
+            for ld in ("auto", "b32"):
+                C = full_rows(run(Ad, Bd, out_device(M, N, ldc, offset=oc), compute=compute, tile=tile,
+                                  fill="piped_ws", stages=S, loader=ld))
+                assert not np.isnan(C[:, :N]).any(), ("ring reported broken", layout, compute, tile, S, ld)
+                assert same_bits(C, ref), (layout, compute, tile, S, ld)
+
+
 def test_deep_ring_copy():
     x = datagen.matrix("normal", datagen.SEED_COPY, 700, 900)
     src = padded_device(x, 904)
