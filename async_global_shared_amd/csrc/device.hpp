@@ -313,16 +313,19 @@ struct CfgMfma256x128 {
 };
 
 // ---- block -> C tile ----------------------------------------------------------
+#ifndef MGEMM_GROUP_ROWS
+#define MGEMM_GROUP_ROWS 4 // tile-rows walked before moving one tile right (fewest L2 misses measured)
+#endif
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b on XCD
 // b % 8), each with its own L2. Give each XCD a contiguous range of logical
-// tiles, then walk the logical order 8 tile-rows down before moving right, so
+// tiles, then walk the logical order a few tile-rows down before moving right, so
 // the blocks resident on one XCD share A and B panels in its L2.
 __device__ inline void block_tile(int bid, int gm, int gn, int &tm, int &tn) {
     const int nb = gm * gn;
     const int x = bid & 7, i = bid >> 3;
     const int q = nb >> 3, r = nb & 7;
     const int lin = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-    constexpr int G = 8;
+    constexpr int G = MGEMM_GROUP_ROWS;
     const int per_group = G * gn;
     const int grp = lin / per_group;
     const int first = grp * G;
