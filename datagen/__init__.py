@@ -174,3 +174,51 @@ def normal01_torch(seed: int, n: int, device="cpu"):
         u2 = lsr(z[1::2], 40).to(torch.float64) * 2.0 ** -24
         out[s:s + c] = (torch.sqrt(-2.0 * torch.log(u1)) * torch.cos(2.0 * np.pi * u2)).to(torch.float32)
     return out
+
+
+# ---- 16-bit inputs (bfloat16 / binary16 bit patterns) ------------------------
+
+def grid_pm1(seed: int, n: int, bits: int) -> np.ndarray:
+    """n values (top `bits` bits of the stream word - 2^(bits-1)) * 2^-(bits-1):
+    a 2^-(bits-1) grid in [-1, 1), exact in any format with >= `bits`
+    significand bits (bits=8 for bfloat16, 11 for binary16)."""
+    def part(s, c):
+        top = (words(seed, s, c) >> np.uint64(64 - bits)).astype(np.int64)
+        return ((top - (1 << (bits - 1))).astype(np.float64) * 2.0 ** -(bits - 1)).astype(np.float32)
+    return _fill(n, part)
+
+
+def to_bits16(x: np.ndarray, fmt: str) -> np.ndarray:
+    """uint16 bit patterns of fp32 values that the format represents exactly
+    ("bf16": upper half of the binary32 pattern; "f16": IEEE binary16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if fmt == "bf16":
+        u = x.view(np.uint32)
+        if np.any(u & np.uint32(0xFFFF)):
+            raise ValueError("value not exact in bfloat16")
+        return (u >> np.uint32(16)).astype(np.uint16)
+    if fmt == "f16":
+        h = x.astype(np.float16)
+        if not np.array_equal(h.astype(np.float32), x, equal_nan=True):
+            raise ValueError("value not exact in binary16")
+        return h.view(np.uint16)
+    raise ValueError(fmt)
+
+
+def matrix16(seed: int, rows: int, cols: int, fmt: str, kind: str = "grid", ld: int | None = None) -> np.ndarray:
+    """rows x ld uint16 bit patterns; [:, :cols] holds the stream's values on the
+    format's grid ("grid"), the 2^-4 grid ("coarse") or ones; padding holds the
+    format's NaN pattern."""
+    ld = cols if ld is None else ld
+    n = rows * cols
+    if kind == "grid":
+        v = grid_pm1(seed, n, 8 if fmt == "bf16" else 11)
+    elif kind == "coarse":
+        v = coarse_pm1(seed, n)
+    elif kind == "ones":
+        v = np.ones(n, np.float32)
+    else:
+        raise ValueError(kind)
+    out = np.full((rows, ld), 0x7FC0 if fmt == "bf16" else 0x7E00, dtype=np.uint16)
+    out[:, :cols] = to_bits16(v, fmt).reshape(rows, cols)
+    return out

@@ -55,6 +55,10 @@ def _bind(lib):
     lib.oracle_copy_f32.argtypes = [i64, i64, fp, i64, fp, i64]
     lib.oracle_copy_f32.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_decode16.argtypes = [ctypes.c_uint16, ctypes.c_int]
+    lib.oracle_decode16.restype = ctypes.c_double
+    lib.oracle_gemm16_f64.argtypes = [i64, i64, i64, fp, i64, fp, i64, dp, i64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_gemm16_f64.restype = None
     return lib
 
 
@@ -92,6 +96,30 @@ def abs_gemm_f64(A: np.ndarray, B: np.ndarray, M=None, N=None, K=None, lib=None)
     C = np.empty((M, N), dtype=np.float64)
     (lib or load()).oracle_abs_gemm_f64(M, N, K, _ptr(A), A.strides[0] // 4,
                                         _ptr(B), B.strides[0] // 4, _ptr(C), N)
+    return C
+
+
+FMT = {"bf16": 1, "f16": 2}
+
+
+def decode16(bits: int, fmt: str, lib=None) -> float:
+    """Value of one 16-bit pattern in format ``fmt`` ("bf16" or "f16")."""
+    return float((lib or load()).oracle_decode16(int(bits) & 0xFFFF, FMT[fmt]))
+
+
+def gemm16_f64(A: np.ndarray, B: np.ndarray, fmt: str, absolute: bool = False, lib=None) -> np.ndarray:
+    """C_ref = dec(A) @ dec(B) in fp64 for uint16 bit-pattern arrays A (M x K)
+    and B (K x N), which may be views with a larger row stride."""
+    for name, x in (("A", A), ("B", B)):
+        if x.dtype != np.uint16 or x.ndim != 2 or (x.size and x.strides[1] != 2):
+            raise TypeError(f"{name} must be a 2-D uint16 array with unit column stride")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    C = np.empty((M, N), dtype=np.float64)
+    (lib or load()).oracle_gemm16_f64(M, N, K, A.ctypes.data, A.strides[0] // 2, B.ctypes.data,
+                                      B.strides[0] // 2, C.ctypes.data, N, FMT[fmt], int(absolute))
     return C
 
 

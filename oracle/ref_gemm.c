@@ -101,3 +101,59 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* ---- 16-bit inputs (bfloat16 / IEEE binary16), fp64 accumulation ---------
+ * The BF16/FP16 form of the same product: A and B hold 16-bit values, the
+ * product and the sum are taken in fp64 as above (every product of two
+ * 16-bit values is exact in fp64), and C is fp64. Formats: fmt 1 = bfloat16
+ * (sign, 8-bit exponent, 7-bit fraction: the upper half of a binary32),
+ * fmt 2 = IEEE 754 binary16 (sign, 5-bit exponent bias 15, 10-bit fraction,
+ * subnormals, infinities, NaN). */
+
+double oracle_decode16(uint16_t h, int fmt)
+{
+    if (fmt == 1) {
+        union { uint32_t u; float f; } v;
+        v.u = (uint32_t)h << 16;
+        return (double)v.f;
+    } else {
+        const int sign = (h >> 15) & 1;
+        const int e = (h >> 10) & 0x1f;
+        const int f = h & 0x3ff;
+        double x;
+        if (e == 0)
+            x = ldexp((double)f, -24);                 /* subnormal: f * 2^-14 * 2^-10 */
+        else if (e == 31)
+            x = f ? NAN : INFINITY;
+        else
+            x = ldexp((double)(f | 0x400), e - 25);    /* (1024 + f) * 2^(e - 15 - 10) */
+        return sign ? -x : x;
+    }
+}
+
+/* C[i*ldc + j] = sum_{p<K} dec(A[i*lda + p]) * dec(B[p*ldb + j]) in fp64,
+ * loop order i, p, j; `absolute` != 0 sums |a| * |b| instead. */
+void oracle_gemm16_f64(int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb,
+                       double *C, int64_t ldc, int fmt, int absolute)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *c = C + i * ldc;
+        int64_t j, p;
+        for (j = 0; j < N; ++j)
+            c[j] = 0.0;
+        for (p = 0; p < K; ++p) {
+            double a = oracle_decode16(A[i * lda + p], fmt);
+            const uint16_t *b = B + p * ldb;
+            if (absolute)
+                a = fabs(a);
+            for (j = 0; j < N; ++j) {
+                const double bv = oracle_decode16(b[j], fmt);
+                c[j] += a * (absolute ? fabs(bv) : bv);
+            }
+        }
+    }
+}

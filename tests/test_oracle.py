@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests import oracle_pins
+from tests import oracle16_pins, oracle_pins
 
 
 @pytest.fixture(scope="module")
@@ -16,7 +16,7 @@ def lib():
     return oracle.load()
 
 
-@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS + oracle16_pins.ALL_PINS16, ids=lambda f: f.__name__)
 def test_pin(lib, pin):
     pin(lib)
 
@@ -38,6 +38,12 @@ MUTANTS = {
     "column_shift": ("c[j] += a * (double)b[j];", "c[j] += a * (double)b[(j + 1) % N];"),
     "abs_drops_sign_of_B": ("a * fabs((double)b[j])", "a * (double)b[j]"),
     "copy_short_row": ("(size_t)cols * sizeof(float)", "(size_t)(cols - 1) * sizeof(float)"),
+    "f16_bias_off_by_one": ("x = ldexp((double)(f | 0x400), e - 25);", "x = ldexp((double)(f | 0x400), e - 24);"),
+    "f16_no_subnormals": ("x = ldexp((double)f, -24);", "x = 0.0;"),
+    "f16_drops_sign": ("return sign ? -x : x;", "return x;"),
+    "bf16_wrong_shift": ("v.u = (uint32_t)h << 16;", "v.u = (uint32_t)h << 15;"),
+    "gemm16_abs_keeps_b_sign": ("c[j] += a * (absolute ? fabs(bv) : bv);", "c[j] += a * bv;"),
+    "gemm16_drops_first_term": ("for (p = 0; p < K; ++p) {\n            double a = oracle_decode16", "for (p = 1; p < K; ++p) {\n            double a = oracle_decode16"),
 }
 
 
@@ -55,7 +61,7 @@ def test_mutant_is_caught(name):
         subprocess.run(["gcc", *oracle.CFLAGS, path, "-o", so, "-lm"], check=True)
         lib = oracle.load(so)
         failed = []
-        for pin in oracle_pins.ALL_PINS:
+        for pin in oracle_pins.ALL_PINS + oracle16_pins.ALL_PINS16:
             try:
                 pin(lib)
             except (AssertionError, ValueError, OverflowError):
