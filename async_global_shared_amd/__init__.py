@@ -24,6 +24,7 @@ COMPUTE_VALU, COMPUTE_MFMA = 0, 1
 TILE_AUTO, TILE_64x64, TILE_128x128, TILE_256x128 = 0, 1, 2, 3
 LOADER_AUTO, LOADER_B128, LOADER_B32 = 0, 1, 2
 OK, ERR_ARG, ERR_ALIAS, ERR_ARCH, ERR_LAUNCH, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+DTYPE_BF16, DTYPE_F16 = 1, 2
 
 _FILL = {"sync": FILL_SYNC, "piped": FILL_PIPED, "piped_ws": FILL_PIPED_WS}
 _COMPUTE = {"valu": COMPUTE_VALU, "mfma": COMPUTE_MFMA}
@@ -63,12 +64,16 @@ def lib():
         L.mgemm_plan_sgemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci,
                                        ctypes.POINTER(Plan)]
         L.mgemm_ring_trace.argtypes = [ci, ci, ci, ci, ctypes.POINTER(ctypes.c_int), ci]
+        L.mgemm_gemm16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, vp]
+        L.mgemm_plan_gemm16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci,
+                                        ctypes.POINTER(Plan)]
         L.mgemm_blocks_per_cu.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci,
                                           ctypes.POINTER(ctypes.c_int)]
         L.mgemm_status_string.argtypes = [ci]
         L.mgemm_status_string.restype = ctypes.c_char_p
         for f in (L.mgemm_sgemm, L.mgemm_sgemm_ex, L.mgemm_tile_copy, L.mgemm_plan_sgemm,
-                  L.mgemm_ring_trace, L.mgemm_version, L.mgemm_blocks_per_cu):
+                  L.mgemm_ring_trace, L.mgemm_version, L.mgemm_blocks_per_cu, L.mgemm_gemm16,
+                  L.mgemm_plan_gemm16):
             f.restype = ci
         _lib = L
     return _lib
@@ -82,6 +87,16 @@ def mgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, stream) -> i
 
 def mgemm_sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader, stream) -> int:
     return lib().mgemm_sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader, stream)
+
+
+def mgemm_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile, stream) -> int:
+    return lib().mgemm_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile, stream)
+
+
+def mgemm_plan_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile):
+    p = Plan()
+    st = lib().mgemm_plan_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile, ctypes.byref(p))
+    return st, p
 
 
 def mgemm_tile_copy(rows, cols, src, lds, dst, ldd, stages, stream) -> int:
@@ -161,6 +176,48 @@ def sgemm(A, B, C=None, *, stages: int = 2, fill: str = "piped", compute: str = 
     if st != OK:
         raise MgemmError(st, "mgemm_sgemm_ex")
     return C
+
+
+def _mat16(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype not in (torch.bfloat16, torch.float16) or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D bfloat16 or float16 torch tensor")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be on a GPU")
+    if t.numel() and t.stride(1) != 1:
+        raise TypeError(f"{name} must have unit column stride")
+    return t.data_ptr(), max(t.stride(0), t.shape[1])
+
+
+def gemm16(A, B, C=None, *, stages: int = 2, fill: str = "piped", tile: str = "auto", stream=None):
+    """C (fp32) = A @ B for bfloat16 or float16 A and B, through mgemm_gemm16."""
+    import torch
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same 16-bit format")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    pa, lda = _mat16(A, "A")
+    pb, ldb = _mat16(B, "B")
+    pc, ldc = _mat(C, "C")
+    dtype = DTYPE_BF16 if A.dtype == torch.bfloat16 else DTYPE_F16
+    st = mgemm_gemm16(M, N, K, pa, lda, pb, ldb, pc, ldc, dtype, stages, _FILL[fill], _TILE[tile], _stream(stream))
+    if st != OK:
+        raise MgemmError(st, "mgemm_gemm16")
+    return C
+
+
+def plan16(M, N, K, *, dtype="bf16", stages=2, fill="piped", tile="auto", lda=None, ldb=None, ldc=None,
+           a_ptr=0x10000, b_ptr=0x40000000, c_ptr=0x80000000):
+    st, p = mgemm_plan_gemm16(M, N, K, a_ptr, K if lda is None else lda, b_ptr, N if ldb is None else ldb, c_ptr,
+                              N if ldc is None else ldc, DTYPE_BF16 if dtype == "bf16" else DTYPE_F16, stages,
+                              _FILL[fill], _TILE[tile])
+    if st != OK:
+        raise MgemmError(st, "mgemm_plan_gemm16")
+    return p.as_dict()
 
 
 def tile_copy(src, dst=None, *, stages: int = 3, stream=None):

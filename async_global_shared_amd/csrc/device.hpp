@@ -129,6 +129,8 @@ template <int BM, int BN, int TM, int TN>
 struct ValuTile {
     using LA = Layout<BM, kBK, SwzA>;
     using LB = Layout<kBK, BN, SwzNone>;
+    // per K slice: A columns and B rows advanced (in 32-bit words / rows), k values
+    static constexpr int A_STEP = kBK, B_STEP = kBK, KPS = kBK, EPW = 1;
     static constexpr int HM = TM / 4, HN = TN / 4;
     static_assert(BM == 64 * HM && BN == 64 * HN, "16 x 16 threads, 4-row groups 64 apart");
     float acc[TM][TN];
@@ -215,6 +217,7 @@ struct MfmaTile {
     static constexpr int BM = 64 * WTM, BN = 64 * WTN;
     using LA = Layout<BM, kBK, SwzA>;
     using LB = Layout<kBK, BN, SwzNone>;
+    static constexpr int A_STEP = kBK, B_STEP = kBK, KPS = kBK, EPW = 1;
     f32x16 acc[WTM][WTN];
     int wm, wn, lane;
 
@@ -290,6 +293,139 @@ struct MfmaTile {
     }
 };
 
+// 16-bit inputs (bfloat16 or binary16), fp32 accumulation: per wave WTM x WTN
+// tiles of 32 x 32 with v_mfma_f32_32x32x16_{bf16,f16}; a K slice is 64
+// elements. A is stored as in the fp32 tiles (rows of the slice, k
+// contiguous): lane l reads its 8 k values A[m][16ks + 8(l/32) + 0..7] as one
+// 16-byte chunk. B stays row-major (k rows, n contiguous) as the fill wrote
+// it; gfx950's transposing LDS read ds_read_b64_tr_b16 turns it into the
+// operand: within each 16-lane group, lane i receives element i%4 of the
+// 8-byte pieces that lanes i/4, 4+i/4, 8+i/4 and 12+i/4 address. If lane q
+// addresses row k0 + q/4, columns nb + 4(q%4) .. +3, lane i receives
+// B[k0 .. k0+3][nb + i], so two such reads give B[16ks + 8(l/32) + 0..7][n],
+// the same k values its A operand holds.
+struct SwzA16 { // rows of 128 B: 16 consecutive rows on distinct 16-byte bank groups
+    MG_HD static constexpr int f(int r) { return (r >> 1) & 7; }
+};
+struct SwzB16 { // the 4 rows of one transposing read on distinct 32-byte bank groups
+    MG_HD static constexpr int f(int r) { return (r & 3) << 1; }
+};
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <int WTM, int WTN, bool BF16>
+struct Mfma16Tile {
+    static constexpr int BM = 64 * WTM, BN = 64 * WTN;
+    static constexpr int KPS = 64, EPW = 2, A_STEP = KPS / EPW, B_STEP = KPS;
+    using LA = Layout<BM, A_STEP, SwzA16>;     // BM rows x 32 words
+    using LB = Layout<KPS, BN / EPW, SwzB16>;  // 64 k rows x BN/2 words
+    f32x16 acc[WTM][WTN];
+    int wm, wn, lane;
+
+    __device__ void init(int tid) {
+        lane = tid & 63;
+        const int w = tid >> 6;
+        wm = w >> 1;
+        wn = w & 1;
+#pragma unroll
+        for (int a = 0; a < WTM; ++a)
+#pragma unroll
+            for (int b = 0; b < WTN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[a][b][i] = 0.0f;
+    }
+    __device__ void poison() {
+#pragma unroll
+        for (int a = 0; a < WTM; ++a)
+#pragma unroll
+            for (int b = 0; b < WTN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[a][b][i] = __builtin_nanf("");
+    }
+
+    // The four transposing reads of one k step (2 column tiles x 2 row
+    // quads) and the wait for them, in one asm block: the compiler's wait
+    // pass does not model ds_read_b64_tr_b16 against in-flight LDS-DMA fills
+    // and would drain the whole prefetch (vmcnt(0)) before it, although the
+    // ring's own wait and barrier already made this slot's slice visible.
+    // The outputs are early-clobber: a read lands while later reads of the
+    // block still need their address registers.
+    template <int OFF0, int OFF1>
+    __device__ static void read_b(unsigned a0, unsigned a1, i16x4 &b00, i16x4 &b01, i16x4 &b10, i16x4 &b11) {
+        asm volatile("ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+                     "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+                     "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+                     "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(b00), "=&v"(b01), "=&v"(b10), "=&v"(b11)
+                     : "v"(a0), "v"(a1), "i"(OFF0), "i"(OFF1));
+    }
+
+    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
+        static_assert(WTN == 2, "read_b covers two 32-column tiles");
+        const int h = lane >> 5, l32 = lane & 31, q = lane & 15, g16 = (lane >> 4) & 1;
+        // lane part of the B read address: row 8h + q/4 of each 16-row k step,
+        // columns n .. n+3 with n = 32(WTN wn + tb) + 16 g16 + 4(q%4); the k
+        // step and the row quad add 16 ks + 4 r2 rows (immediate offsets: the
+        // swizzle depends on the row mod 4 only)
+        unsigned ab[WTN];
+        const unsigned bs = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)Bs;
+#pragma unroll
+        for (int tb = 0; tb < WTN; ++tb) {
+            const int k = 8 * h + (q >> 2);
+            const int n = 32 * WTN * wn + 32 * tb + 16 * g16 + 4 * (q & 3);
+            ab[tb] = bs + LB::pos(k, n >> 3) * 16 + (n & 7) * 2;
+        }
+        static_for<0, KPS / 16>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
+            u32x4 a[WTM];
+#pragma unroll
+            for (int ta = 0; ta < WTM; ++ta) {
+                const int m = 32 * WTM * wm + 32 * ta + l32;
+                a[ta] = *(const u32x4 *)(As + LA::pos(m, 2 * ks + h) * 16);
+            }
+            i16x4 b[WTN][2];
+            read_b<(16 * ks) * LB::CPR * 16, (16 * ks + 4) * LB::CPR * 16>(ab[0], ab[1], b[0][0], b[0][1], b[1][0],
+                                                                            b[1][1]);
+#pragma unroll
+            for (int ta = 0; ta < WTM; ++ta)
+#pragma unroll
+                for (int tb = 0; tb < WTN; ++tb) {
+                    const i16x4 lo = b[tb][0], hi = b[tb][1];
+                    typedef short i16x8 __attribute__((ext_vector_type(8)));
+                    const i16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    if constexpr (BF16)
+                        acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, a[ta]), __builtin_bit_cast(bf16x8, bv), acc[ta][tb], 0, 0, 0);
+                    else
+                        acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(f16x8, a[ta]), __builtin_bit_cast(f16x8, bv), acc[ta][tb], 0, 0, 0);
+                }
+        });
+    }
+
+    __device__ void store(float *C, int ldc, int m0, int n0, int M, int N, bool) const {
+        const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int ta = 0; ta < WTM; ++ta)
+#pragma unroll
+            for (int tb = 0; tb < WTN; ++tb) {
+                const int c = n0 + 32 * WTN * wn + 32 * tb + l32;
+                if (c >= N)
+                    continue;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = m0 + 32 * WTM * wm + 32 * ta + (i >> 2) * 8 + h * 4 + (i & 3);
+                    if (r < M)
+                        C[(size_t)r * ldc + c] = acc[ta][tb][i];
+                }
+            }
+    }
+};
+
 // Tile configurations (block tile, compute tile).
 struct CfgValu64 {
     using Tile = ValuTile<64, 64, 4, 4>;
@@ -309,6 +445,16 @@ struct CfgMfma128 {
 };
 struct CfgMfma256x128 {
     using Tile = MfmaTile<4, 2>;
+    static constexpr int BM = 256, BN = 128;
+};
+template <bool BF16>
+struct CfgH128 {
+    using Tile = Mfma16Tile<2, 2, BF16>;
+    static constexpr int BM = 128, BN = 128;
+};
+template <bool BF16>
+struct CfgH256x128 {
+    using Tile = Mfma16Tile<4, 2, BF16>;
     static constexpr int BM = 256, BN = 128;
 };
 
@@ -348,6 +494,8 @@ __device__ inline void wait_vm() {
 // Block barrier after this wave's LDS reads and writes have completed.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// A and B are addressed as 32-bit words (fp32 elements, or pairs of 16-bit
+// elements); lda and ldb are in words, a_cols is the row extent of A in words.
 struct GemmArgs {
     const float *A;
     const float *B;
@@ -356,6 +504,7 @@ struct GemmArgs {
     int lda, ldb, ldc;
     int gm, gn;
     int vec_store;
+    int a_cols;
 };
 
 template <int W>
@@ -382,13 +531,15 @@ struct GemmCtx {
     unsigned char *smem;
     int wave, lane;
     const float *Ablk; // A + m0 * lda
-    const float *Bblk; // B + n0
-    int ldb, K, a_rows, b_cols;
+    const float *Bblk; // B + n0 (in words)
+    int ldb, K, a_cols, a_rows, b_cols;
 
-    // slice s covers A[m0.., 16s..] and B[16s.., n0..]; limits are relative
-    __device__ const float *a_ptr(int s) const { return Ablk + s * kBK; }
-    __device__ const float *b_ptr(int s) const { return Bblk + (size_t)s * kBK * ldb; }
-    __device__ int klim(int s) const { return K - s * kBK; }
+    // slice s covers A[m0.., s*A_STEP..] and B[s*B_STEP.., n0..] (words / rows);
+    // the limits are relative to the slice
+    __device__ const float *a_ptr(int s) const { return Ablk + s * Tile::A_STEP; }
+    __device__ const float *b_ptr(int s) const { return Bblk + (size_t)s * Tile::B_STEP * ldb; }
+    __device__ int a_klim(int s) const { return a_cols - s * Tile::A_STEP; }
+    __device__ int b_klim(int s) const { return K - s * Tile::B_STEP; }
     __device__ void barrier() { lds_barrier(); }
     __device__ void compute(int, int slot) {
         const unsigned char *base = smem + slot * SLOT;
@@ -403,17 +554,17 @@ struct PipedOps : GemmCtx<Tile, W> {
     __device__ void issue(int s, int slot) {
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
-        const int k = this->klim(s);
+        const int ka = this->a_klim(s), kb = this->b_klim(s);
         unsigned char *base = this->smem + slot * C::SLOT;
 #pragma unroll
         for (int i = 0; i < C::OA::U; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t *)(base + C::OA::lds_off(i, this->wave)), W,
-                                                      this->oa.voff(i, this->a_rows, k), 0, 0, 0);
+                                                      this->oa.voff(i, this->a_rows, ka), 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < C::OB::U; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (lds_t *)(base + C::LA::BYTES + C::OB::lds_off(i, this->wave)), W,
-                this->ob.voff(i, k, this->b_cols), 0, 0, 0);
+                this->ob.voff(i, kb, this->b_cols), 0, 0, 0);
     }
     // each slice is OA::U + OB::U fill instructions of this wave
     template <int P>
@@ -440,13 +591,13 @@ struct SyncOps : GemmCtx<Tile, W> {
     __device__ void load(int s) {
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
-        const int k = this->klim(s);
+        const int ka = this->a_klim(s), kb = this->b_klim(s);
 #pragma unroll
         for (int i = 0; i < C::OA::U; ++i)
-            va[SET][i] = ld(ra, this->oa.voff(i, this->a_rows, k));
+            va[SET][i] = ld(ra, this->oa.voff(i, this->a_rows, ka));
 #pragma unroll
         for (int i = 0; i < C::OB::U; ++i)
-            vb[SET][i] = ld(rb, this->ob.voff(i, k, this->b_cols));
+            vb[SET][i] = ld(rb, this->ob.voff(i, kb, this->b_cols));
     }
     template <int SET>
     __device__ void store(int slot) {
@@ -470,7 +621,7 @@ __global__ void __launch_bounds__(kThreads) sgemm_kernel(GemmArgs g) {
     block_tile(blockIdx.x, g.gm, g.gn, tm, tn);
     const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
     const int tid = threadIdx.x;
-    const int T = (g.K + kBK - 1) / kBK;
+    const int T = (g.K + Tile::KPS - 1) / Tile::KPS;
 
     using Ops = typename std::conditional<PIPED, PipedOps<Tile, W>, SyncOps<Tile, W, (S > 1 ? S - 1 : 1)>>::type;
     Ops ops;
@@ -478,11 +629,12 @@ __global__ void __launch_bounds__(kThreads) sgemm_kernel(GemmArgs g) {
     ops.lane = tid & 63;
     ops.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     ops.Ablk = g.A + (size_t)m0 * g.lda;
-    ops.Bblk = g.B + n0;
+    ops.Bblk = g.B + n0 / Tile::EPW;
     ops.ldb = g.ldb;
     ops.K = g.K;
+    ops.a_cols = g.a_cols;
     ops.a_rows = g.M - m0;
-    ops.b_cols = g.N - n0;
+    ops.b_cols = (g.N - n0) / Tile::EPW;
     ops.oa.init(ops.lane, ops.wave, g.lda);
     ops.ob.init(ops.lane, ops.wave, g.ldb);
     ops.tile.init(tid);
@@ -563,17 +715,18 @@ __global__ void __launch_bounds__(kWsThreads) sgemm_ws_kernel(GemmArgs g) {
     int tm, tn;
     block_tile(blockIdx.x, g.gm, g.gn, tm, tn);
     const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
-    const int T = (g.K + kBK - 1) / kBK;
+    const int T = (g.K + Tile::KPS - 1) / Tile::KPS;
 
     Ops ops;
     ops.smem = smem;
     ops.lane = lane;
     ops.Ablk = g.A + (size_t)m0 * g.lda;
-    ops.Bblk = g.B + n0;
+    ops.Bblk = g.B + n0 / Tile::EPW;
     ops.ldb = g.ldb;
     ops.K = g.K;
+    ops.a_cols = g.a_cols;
     ops.a_rows = g.M - m0;
-    ops.b_cols = g.N - n0;
+    ops.b_cols = (g.N - n0) / Tile::EPW;
 
     if (wave >= kWsCompute) {
         // filling wave f: the fills of unit split f of every slice

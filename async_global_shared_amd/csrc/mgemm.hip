@@ -21,7 +21,7 @@ using namespace mgemm;
 
 namespace {
 
-constexpr int64_t kMaxLd = int64_t(1) << 22;     // keeps every in-block byte offset below 2^31
+constexpr int64_t kMaxLd = int64_t(1) << 21;     // 256 rows x 2^21 words x 4 B: in-block byte offsets stay below 2^31
 constexpr int64_t kMaxExtent = int64_t(1) << 31; // rows * ld per operand, in elements
 constexpr int64_t kAutoBigTileBlocks = 512;      // 128x128 tiles once they give >= 2 blocks per CU
 
@@ -161,6 +161,16 @@ MG_GEMM_CFG(CfgValu128)
 MG_GEMM_CFG(CfgMfma64)
 MG_GEMM_CFG(CfgMfma128)
 MG_GEMM_CFG(CfgMfma256x128)
+#define MG_GEMM16_INST(CFG, S, W)                                                                        \
+    template __global__ void mgemm::sgemm_kernel<mgemm::CFG, S, true, W>(mgemm::GemmArgs);               \
+    template __global__ void mgemm::sgemm_kernel<mgemm::CFG, S, false, W>(mgemm::GemmArgs);
+#define MG_GEMM16_CFG(CFG)                                                                               \
+    MG_GEMM16_INST(CFG, 1, 16) MG_GEMM16_INST(CFG, 2, 16) MG_GEMM16_INST(CFG, 3, 16)                     \
+    MG_GEMM16_INST(CFG, 1, 4) MG_GEMM16_INST(CFG, 2, 4) MG_GEMM16_INST(CFG, 3, 4)
+MG_GEMM16_CFG(CfgH128<true>)
+MG_GEMM16_CFG(CfgH128<false>)
+MG_GEMM16_CFG(CfgH256x128<true>)
+MG_GEMM16_CFG(CfgH256x128<false>)
 #define MG_COPY_INST(S)                                                                                  \
     template __global__ void mgemm::tile_copy_kernel<S, 16, true>(mgemm::CopyArgs);                      \
     template __global__ void mgemm::tile_copy_kernel<S, 16, false>(mgemm::CopyArgs);                     \
@@ -232,6 +242,88 @@ int launch(const void *fn, int blocks, void *arg, hipStream_t stream, int thread
     void *args[] = {arg};
     const hipError_t e = hipLaunchKernel(fn, dim3(blocks), dim3(threads), args, 0, stream);
     return e == hipSuccess ? MGEMM_OK : MGEMM_ERR_LAUNCH;
+}
+
+// ---- 16-bit GEMM -------------------------------------------------------------------
+
+int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                const float *C, int64_t ldc, int dtype, int stages, int fill, int tile, mgemm_plan_t *pl) {
+    if (M < 0 || N < 0 || K < 0 || (dtype != MGEMM_DTYPE_BF16 && dtype != MGEMM_DTYPE_F16) || stages < 1 ||
+        stages > kMaxSyncStages || (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED) ||
+        (tile != MGEMM_TILE_AUTO && tile != MGEMM_TILE_128x128 && tile != MGEMM_TILE_256x128))
+        return MGEMM_ERR_ARG;
+    // the loaders move 32-bit words: pairs of 16-bit elements along k (A) and n (B)
+    // (an empty operand is never read: its base and leading dimension are free)
+    const bool a_used = M > 0 && K > 0, b_used = K > 0 && N > 0;
+    if (K % 2 || N % 2 || (a_used && (lda % 2 || (reinterpret_cast<uintptr_t>(A) & 3))) ||
+        (b_used && (ldb % 2 || (reinterpret_cast<uintptr_t>(B) & 3))))
+        return MGEMM_ERR_ARG;
+    int st;
+    if ((st = check_matrix(A, M, K / 2, lda / 2)) != MGEMM_OK || (st = check_matrix(B, K, N / 2, ldb / 2)) != MGEMM_OK ||
+        (st = check_matrix(C, M, N, ldc)) != MGEMM_OK)
+        return st;
+    if (M > 0 && K > 0 && lda < K)
+        return MGEMM_ERR_ARG;
+    if (M >= kMaxExtent || N >= kMaxExtent || K >= kMaxExtent)
+        return MGEMM_ERR_UNSUPPORTED;
+    const Range rc = span(C, M, N, ldc);
+    if (overlap(rc, span(A, M, K / 2, lda / 2)) || overlap(rc, span(B, K, N / 2, ldb / 2)))
+        return MGEMM_ERR_ALIAS;
+    const bool b128_ok = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 && N % 8 == 0;
+    const int W = b128_ok ? 16 : 4;
+    if (tile == MGEMM_TILE_AUTO)
+        tile = ((M + 255) / 256) * ((N + 127) / 128) >= 1024 ? MGEMM_TILE_256x128 : MGEMM_TILE_128x128;
+    const int bm = tile == MGEMM_TILE_256x128 ? 256 : 128, bn = 128;
+    constexpr int kps = 64;
+    mgemm_plan_t p;
+    std::memset(&p, 0, sizeof p);
+    p.compute = MGEMM_COMPUTE_MFMA;
+    p.tile = tile;
+    p.bm = bm;
+    p.bn = bn;
+    p.bk = kps;
+    p.threads = kThreads;
+    p.blocks = (int)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
+    p.load_bytes = W;
+    p.slices = (int)((K + kps - 1) / kps);
+    p.stages = stages;
+    p.fill_mode = fill;
+    const int slice_bytes = (bm * kps + kps * bn) * 2;
+    p.lds_bytes = stages * slice_bytes;
+    p.loads_per_slice = slice_bytes / (64 * W) / kWaves;
+    p.max_vmcnt = fill == MGEMM_FILL_PIPED ? std::min(63, std::max(0, stages - 2) * p.loads_per_slice) : 0;
+    if (pl)
+        *pl = p;
+    return MGEMM_OK;
+}
+
+template <class Cfg, int S, int W>
+const void *gk16(int fill) {
+    return fill == MGEMM_FILL_SYNC ? (const void *)&sgemm_kernel<Cfg, S, false, W>
+                                   : (const void *)&sgemm_kernel<Cfg, S, true, W>;
+}
+template <class Cfg, int W>
+const void *gemm16_kernel_w(int S, int fill) {
+    switch (S) {
+    case 1: return gk16<Cfg, 1, W>(fill);
+    case 2: return gk16<Cfg, 2, W>(fill);
+    default: return gk16<Cfg, 3, W>(fill);
+    }
+}
+const void *select_gemm16(const mgemm_plan_t &p, int dtype) {
+    const bool big = p.tile == MGEMM_TILE_256x128, w16 = p.load_bytes == 16;
+    if (dtype == MGEMM_DTYPE_BF16) {
+        if (big)
+            return w16 ? gemm16_kernel_w<CfgH256x128<true>, 16>(p.stages, p.fill_mode)
+                       : gemm16_kernel_w<CfgH256x128<true>, 4>(p.stages, p.fill_mode);
+        return w16 ? gemm16_kernel_w<CfgH128<true>, 16>(p.stages, p.fill_mode)
+                   : gemm16_kernel_w<CfgH128<true>, 4>(p.stages, p.fill_mode);
+    }
+    if (big)
+        return w16 ? gemm16_kernel_w<CfgH256x128<false>, 16>(p.stages, p.fill_mode)
+                   : gemm16_kernel_w<CfgH256x128<false>, 4>(p.stages, p.fill_mode);
+    return w16 ? gemm16_kernel_w<CfgH128<false>, 16>(p.stages, p.fill_mode)
+               : gemm16_kernel_w<CfgH128<false>, 4>(p.stages, p.fill_mode);
 }
 
 // ---- host recorder for mgemm_ring_trace ----------------------------------------------
@@ -316,6 +408,7 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     g.gm = (int)((M + p.bm - 1) / p.bm);
     g.gn = (int)((N + p.bn - 1) / p.bn);
     g.vec_store = aligned16(C) && ldc % 4 == 0;
+    g.a_cols = (int)K;
     return launch(select_gemm(p), p.blocks, &g, s, p.threads);
 }
 
@@ -323,6 +416,49 @@ int mgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
                 float *C, int64_t ldc, int stages, int fill_mode, void *stream) {
     return mgemm_sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, MGEMM_COMPUTE_VALU, MGEMM_TILE_AUTO,
                           MGEMM_LOADER_AUTO, stream);
+}
+
+int mgemm_plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                      const float *C, int64_t ldc, int dtype, int stages, int fill_mode, int tile,
+                      mgemm_plan_t *plan) {
+    return plan_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile, plan);
+}
+
+int mgemm_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb, float *C,
+                 int64_t ldc, int dtype, int stages, int fill_mode, int tile, void *stream) {
+    mgemm_plan_t p;
+    int st = plan_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile, &p);
+    if (st != MGEMM_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return MGEMM_OK;
+    int dev;
+    if ((st = current_device(&dev)) != MGEMM_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (K == 0) {
+        const int64_t n = M * N;
+        const int blocks = (int)std::min<int64_t>((n + kThreads - 1) / kThreads, 4096);
+        int m = (int)M, nn = (int)N, l = (int)ldc;
+        void *args[] = {&C, &m, &nn, &l};
+        const hipError_t e = hipLaunchKernel((const void *)&zero_kernel, dim3(blocks), dim3(kThreads), args, 0, s);
+        return e == hipSuccess ? MGEMM_OK : MGEMM_ERR_LAUNCH;
+    }
+    GemmArgs g;
+    g.A = static_cast<const float *>(A);
+    g.B = static_cast<const float *>(B);
+    g.C = C;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.lda = (int)(lda / 2);
+    g.ldb = (int)(ldb / 2);
+    g.ldc = (int)ldc;
+    g.gm = (int)((M + p.bm - 1) / p.bm);
+    g.gn = (int)((N + p.bn - 1) / p.bn);
+    g.vec_store = 0;
+    g.a_cols = (int)(K / 2);
+    return launch(select_gemm16(p, dtype), p.blocks, &g, s, p.threads);
 }
 
 int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, float *dst, int64_t ldd, int stages,

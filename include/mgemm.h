@@ -29,8 +29,10 @@
  *  - Arguments are validated before any HIP call; a non-OK status means
  *    nothing was enqueued. No entry point exits the process.
  *  - C must not overlap A or B (the pages' kernels take __restrict__ inputs).
- *  - Each operand extent (rows x ld) must stay below 2^31 elements and every
- *    ld below 2^22; larger problems return MGEMM_ERR_UNSUPPORTED.
+ *  - Each operand extent (rows x ld) must stay below 2^31 32-bit words and
+ *    every ld below 2^21 words (2^22 elements of a 16-bit operand), so that
+ *    every byte offset inside a 256-row block tile fits the buffer loads'
+ *    31-bit range; larger problems return MGEMM_ERR_UNSUPPORTED.
  */
 #ifndef MGEMM_H
 #define MGEMM_H
@@ -40,6 +42,8 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+struct mgemm_plan; /* defined below (mgemm_plan_t) */
 
 #define MGEMM_VERSION 100 /* 1.0.0 */
 
@@ -98,6 +102,36 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K,
                    float *C, int64_t ldc,
                    int stages, int fill_mode, int compute, int tile, int loader,
                    void *stream);
+
+/* element formats of mgemm_gemm16 */
+#define MGEMM_DTYPE_BF16 1 /* bfloat16: the upper half of a binary32 */
+#define MGEMM_DTYPE_F16 2  /* IEEE 754 binary16 */
+
+/*
+ * C[0:M, 0:N] = A[0:M, 0:K] * B[0:K, 0:N] for 16-bit A and B (dtype
+ * MGEMM_DTYPE_BF16 or MGEMM_DTYPE_F16, the same format for both) and fp32 C:
+ * the tensor-core GEMM "fed by the same pipeline" that the day-74 lesson
+ * points to for a later lesson, here v_mfma_f32_32x32x16_{bf16,f16} on the
+ * same asynchronous LDS ring (64-element K slices). Products and sums are
+ * fp32 inside the MFMA. lda and ldb count 16-bit elements, ldc fp32
+ * elements. Requirements (else MGEMM_ERR_ARG): K, N, lda and ldb even; A and
+ * B 4-byte aligned. stages 1 .. 3; fill_mode MGEMM_FILL_SYNC or
+ * MGEMM_FILL_PIPED (bit-identical results); tile MGEMM_TILE_AUTO,
+ * MGEMM_TILE_128x128 or MGEMM_TILE_256x128. Other conventions as mgemm_sgemm.
+ */
+int mgemm_gemm16(int64_t M, int64_t N, int64_t K,
+                 const void *A, int64_t lda,
+                 const void *B, int64_t ldb,
+                 float *C, int64_t ldc,
+                 int dtype, int stages, int fill_mode, int tile, void *stream);
+
+/* The launch mgemm_gemm16 would make (no device access); as mgemm_plan_sgemm. */
+int mgemm_plan_gemm16(int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t lda,
+                      const void *B, int64_t ldb,
+                      const float *C, int64_t ldc,
+                      int dtype, int stages, int fill_mode, int tile,
+                      struct mgemm_plan *plan);
 
 /*
  * dst[0:rows, 0:cols] = src[0:rows, 0:cols], streamed global -> LDS -> global

@@ -55,11 +55,24 @@ def sg(M=64, N=64, K=64, A=A0, lda=None, B=B0, ldb=None, C=C0, ldc=None, stages=
     (dict(lda=63), m.ERR_ARG), (dict(ldb=10), m.ERR_ARG), (dict(ldc=63), m.ERR_ARG),
     (dict(A=0), m.ERR_ARG), (dict(B=0), m.ERR_ARG), (dict(C=0), m.ERR_ARG),
     (dict(C=A0), m.ERR_ALIAS), (dict(C=B0 + 4 * 100), m.ERR_ALIAS),
-    (dict(lda=1 << 22), m.ERR_UNSUPPORTED), (dict(M=1 << 20, K=4096), m.ERR_UNSUPPORTED),
+    (dict(lda=1 << 21), m.ERR_UNSUPPORTED), (dict(M=1 << 20, K=4096), m.ERR_UNSUPPORTED),
     (dict(A=A0 + 4, loader=1), m.ERR_ARG), (dict(K=62, loader=1), m.ERR_ARG),
 ])
 def test_validation_before_any_device_call(kw, want):
     assert sg(**kw) == want
+
+
+def test_largest_leading_dimension_is_planned():
+    # 256-row tiles at ld = 2^21 - 4 words: the last in-block byte offset,
+    # 255 * ld * 4 + ..., still fits below 2^31 (planner only: no device access)
+    ld = (1 << 21) - 4
+    A, B, C = 1 << 32, 1 << 36, 1 << 40
+    st, p = m.mgemm_plan_sgemm(256, 64, 64, A, ld, B, 64, C, 64, 2, 1, 1, 3, 0)
+    assert st == m.OK and p.bm == 256 and 255 * ld * 4 + 64 * 4 < 1 << 31
+    st, p = m.mgemm_plan_gemm16(256, 64, 64, A, 2 * ld, B, 64, C, 64, 1, 2, 1, 3)
+    assert st == m.OK and p.bm == 256
+    st, _ = m.mgemm_plan_gemm16(256, 64, 64, A, 2 * ld + 8, B, 64, C, 64, 1, 2, 1, 3)
+    assert st == m.ERR_UNSUPPORTED
 
 
 def test_empty_operands_need_no_pointers():
@@ -428,3 +441,88 @@ def test_isa_warp_specialised(isa, cfg):
             assert "ds_add_u32" in body and "s_sleep" in body
             assert re.search(r"buffer_load_dword\S* .* lds", body)
             assert "flat_atomic" not in body and "flat_load" not in body
+
+
+# ---- 16-bit (bfloat16 / binary16) GEMM: validation, plans, ISA ----------------
+
+def g16(M=64, N=64, K=64, A=A0, lda=None, B=B0, ldb=None, C=C0, ldc=None, dtype=1, stages=2, fill=1, tile=0):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return m.mgemm_plan_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill, tile)[0]
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=0), m.ERR_ARG), (dict(dtype=3), m.ERR_ARG), (dict(stages=0), m.ERR_ARG), (dict(stages=4), m.ERR_ARG),
+    (dict(fill=2), m.ERR_ARG), (dict(tile=1), m.ERR_ARG), (dict(tile=4), m.ERR_ARG),
+    (dict(K=63, lda=64), m.ERR_ARG), (dict(N=63, ldb=64, ldc=64), m.ERR_ARG), (dict(lda=65), m.ERR_ARG),
+    (dict(ldb=65), m.ERR_ARG), (dict(A=A0 + 2), m.ERR_ARG), (dict(B=B0 + 6), m.ERR_ARG), (dict(lda=62), m.ERR_ARG),
+    (dict(ldc=63), m.ERR_ARG), (dict(A=0), m.ERR_ARG), (dict(C=0), m.ERR_ARG),
+    (dict(C=A0), m.ERR_ALIAS), (dict(C=B0 + 2 * 64 * 63), m.ERR_ALIAS), (dict(C=A0 + 2 * 64 * 64), m.OK),
+    (dict(lda=1 << 22), m.ERR_UNSUPPORTED),
+    (dict(A=A0 + 4), m.OK), (dict(B=B0 + 4, ldb=66), m.OK), (dict(stages=3, fill=0, tile=3), m.OK),
+])
+def test_gemm16_validation(kw, want):
+    assert g16(**kw) == want
+    if want != m.OK:
+        # the launching entry point refuses the same arguments before any HIP call
+        a = dict(M=64, N=64, K=64, A=A0, B=B0, C=C0, dtype=1, stages=2, fill=1, tile=0)
+        a.update(kw)
+        a.setdefault("lda", a["K"]), a.setdefault("ldb", a["N"]), a.setdefault("ldc", a["N"])
+        assert m.mgemm_gemm16(a["M"], a["N"], a["K"], a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"],
+                              a["dtype"], a["stages"], a["fill"], a["tile"], None) == want
+
+
+def test_gemm16_empty_operands_ignore_layout():
+    # an operand with no elements is never read: its base and ld are free
+    assert g16(M=10, K=0, lda=1, N=12, B=0, ldb=1, ldc=13) == m.OK
+    assert g16(M=0, K=64, A=0, lda=1) == m.OK
+    assert m.mgemm_gemm16(0, 8, 8, 0, 1, B0, 8, 0, 8, 1, 2, 1, 0, None) == m.OK
+
+
+def test_gemm16_plans():
+    p = m.plan16(8192, 8192, 8192)
+    assert (p["bm"], p["bn"], p["bk"], p["blocks"], p["load_bytes"]) == (256, 128, 64, 32 * 64, 16)
+    assert p["slices"] == 128 and p["lds_bytes"] == 2 * (256 + 128) * 64 * 2 and p["compute"] == m.COMPUTE_MFMA
+    # one slice: (256 x 64 + 64 x 128) 16-bit elements = 48 KiB = 12 dwordx4 per lane of each of 4 waves
+    assert p["loads_per_slice"] == 12 and p["max_vmcnt"] == 0
+    assert m.plan16(8192, 8192, 8192, stages=3)["max_vmcnt"] == 12
+    assert m.plan16(8192, 8192, 8192, stages=3, tile="256x128")["lds_bytes"] == 3 * 49152 <= 160 * 1024
+    p = m.plan16(1024, 1024, 1024, dtype="f16")
+    assert (p["bm"], p["blocks"]) == (128, 64)
+    # ragged K or a leading dimension off the 8-element grid -> 4-byte loads (pairs of elements)
+    p = m.plan16(300, 258, 198, stages=3)
+    assert p["load_bytes"] == 4 and p["slices"] == 4 and p["loads_per_slice"] == 32 and p["max_vmcnt"] == 32
+    assert m.plan16(300, 264, 200, lda=208, ldb=272)["load_bytes"] == 16
+    assert m.plan16(64, 64, 64, a_ptr=0x10004)["load_bytes"] == 4
+
+
+def _name16(cfg, bf16, S, piped, W):
+    return f"_ZN5mgemm12sgemm_kernelINS_{len(cfg)}{cfg}ILb{int(bf16)}EEELi{S}ELb{int(piped)}ELi{W}EEEvNS_8GemmArgsE"
+
+
+@pytest.mark.parametrize("cfg", ["CfgH128", "CfgH256x128"])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_isa_gemm16(isa, cfg, bf16):
+    """The 16-bit kernels multiply on v_mfma_f32_32x32x16_{bf16,f16}, read B
+    through the transposing LDS read, fill LDS asynchronously (piped) or
+    through VGPRs (sync), and never drain the prefetch before the MFMAs."""
+    mfma = "v_mfma_f32_32x32x16_" + ("bf16" if bf16 else "f16")
+    per_slice = {"CfgH128": 4 * 4, "CfgH256x128": 8 * 4}[cfg]  # WTM*WTN tiles x 4 k-steps per slice
+    for S in (1, 2, 3):
+        for W in (16, 4):
+            for piped in (True, False):
+                lines = isa[_name16(cfg, bf16, S, piped, W)]
+                body = "\n".join(lines)
+                assert body.count(mfma) >= per_slice, (cfg, S, W, piped)
+                assert "v_mfma_f32_32x32x2_f32" not in body
+                assert "ds_read_b64_tr_b16" in body and "ds_read_b128" in body
+                width = "dwordx4" if W == 16 else "dword"
+                if piped:
+                    assert re.search(rf"buffer_load_{width} .* lds", body) and "ds_write" not in body
+                    if S >= 2:
+                        drained, reached = _drain_before_compute(lines, mfma)
+                        assert reached and not drained, (cfg, S, W)
+                else:
+                    assert "ds_write" in body and not re.search(r"buffer_load\S* .* lds", body)
+                assert "v_pk_fma_f32" not in body and "v_pk_add_f32" not in body and "v_pk_mul_f32" not in body
