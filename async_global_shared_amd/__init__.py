@@ -21,14 +21,14 @@ ISA_PATH = os.path.join(_HERE, "_build", "mgemm-gfx950.s")
 MGEMM_VERSION = 100
 FILL_SYNC, FILL_PIPED, FILL_PIPED_WS = 0, 1, 2
 COMPUTE_VALU, COMPUTE_MFMA = 0, 1
-TILE_AUTO, TILE_64x64, TILE_128x128, TILE_256x128 = 0, 1, 2, 3
+TILE_AUTO, TILE_64x64, TILE_128x128, TILE_256x128, TILE_256x256 = 0, 1, 2, 3, 4
 LOADER_AUTO, LOADER_B128, LOADER_B32 = 0, 1, 2
 OK, ERR_ARG, ERR_ALIAS, ERR_ARCH, ERR_LAUNCH, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 DTYPE_BF16, DTYPE_F16 = 1, 2
 
 _FILL = {"sync": FILL_SYNC, "piped": FILL_PIPED, "piped_ws": FILL_PIPED_WS}
 _COMPUTE = {"valu": COMPUTE_VALU, "mfma": COMPUTE_MFMA}
-_TILE = {"auto": TILE_AUTO, "64x64": TILE_64x64, "128x128": TILE_128x128, "256x128": TILE_256x128}
+_TILE = {"auto": TILE_AUTO, "64x64": TILE_64x64, "128x128": TILE_128x128, "256x128": TILE_256x128, "256x256": TILE_256x256}
 _LOADER = {"auto": LOADER_AUTO, "b128": LOADER_B128, "b32": LOADER_B32}
 
 

@@ -38,6 +38,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+constexpr int kLdsBytes = 160 * 1024; // LDS per CU (and per workgroup) on gfx950
 constexpr int kWaves = 4;
 constexpr int kBK = 16;
 // Every buffer descriptor spans 2^31 bytes from its (per-block, per-slice)
@@ -75,7 +76,7 @@ struct Layout {
     static constexpr int CPR = COLS / 4;
     static constexpr int CHUNKS = ROWS * CPR;
     static constexpr int BYTES = CHUNKS * 16;
-    static_assert(COLS % 4 == 0 && CHUNKS % (64 * kWaves) == 0, "whole wave instructions per slice");
+    static_assert(COLS % 4 == 0, "whole 16-byte chunks per row");
     MG_HD static constexpr int pos(int r, int c4) { return r * CPR + (c4 ^ Swz::f(r)); }
     MG_HD static constexpr int row(int p) { return p / CPR; }
     MG_HD static constexpr int col4(int p) { return (p % CPR) ^ Swz::f(p / CPR); }
@@ -92,6 +93,7 @@ template <class L, int W, int WAVES = kWaves>
 struct Operand {
     static constexpr int U = (W == 16) ? L::CHUNKS / (64 * WAVES) : (L::CHUNKS * 4) / (64 * WAVES);
     static_assert(W == 16 || W == 4, "load width");
+    static_assert(L::CHUNKS % (64 * WAVES) == 0, "whole wave instructions per slice");
     int rr[U], cc[U], off[U];
 
     __device__ void init(int lane, int wave, int ld) {
@@ -130,7 +132,7 @@ struct ValuTile {
     using LA = Layout<BM, kBK, SwzA>;
     using LB = Layout<kBK, BN, SwzNone>;
     // per K slice: A columns and B rows advanced (in 32-bit words / rows), k values
-    static constexpr int A_STEP = kBK, B_STEP = kBK, KPS = kBK, EPW = 1;
+    static constexpr int A_STEP = kBK, B_STEP = kBK, KPS = kBK, EPW = 1, WAVES = kWaves;
     static constexpr int HM = TM / 4, HN = TN / 4;
     static_assert(BM == 64 * HM && BN == 64 * HN, "16 x 16 threads, 4-row groups 64 apart");
     float acc[TM][TN];
@@ -217,7 +219,7 @@ struct MfmaTile {
     static constexpr int BM = 64 * WTM, BN = 64 * WTN;
     using LA = Layout<BM, kBK, SwzA>;
     using LB = Layout<kBK, BN, SwzNone>;
-    static constexpr int A_STEP = kBK, B_STEP = kBK, KPS = kBK, EPW = 1;
+    static constexpr int A_STEP = kBK, B_STEP = kBK, KPS = kBK, EPW = 1, WAVES = kWaves;
     f32x16 acc[WTM][WTN];
     int wm, wn, lane;
 
@@ -307,27 +309,39 @@ struct MfmaTile {
 struct SwzA16 { // rows of 128 B: 16 consecutive rows on distinct 16-byte bank groups
     MG_HD static constexpr int f(int r) { return (r >> 1) & 7; }
 };
-struct SwzB16 { // the 4 rows of one transposing read on distinct 32-byte bank groups
-    MG_HD static constexpr int f(int r) { return (r & 3) << 1; }
+#ifndef MGEMM_SWZB16
+#define MGEMM_SWZB16 2
+#endif
+struct SwzB16 { // the 4 rows of one transposing read on distinct 64-byte bank groups
+    MG_HD static constexpr int f(int r) { return (r & 3) << MGEMM_SWZB16; }
 };
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-template <int WTM, int WTN, bool BF16>
+// K elements per slice of the 16-bit tiles: 64 (rows of 128 B) or 32 (rows
+// of 64 B, the fp32 tiles' row size, half the LDS per stage)
+#ifndef MGEMM_K16
+#define MGEMM_K16 64
+#endif
+constexpr int kK16 = MGEMM_K16;
+static_assert(kK16 == 32 || kK16 == 64, "16-bit K slice");
+
+// WGM x WGN waves, each WTM x WTN tiles of 32 x 32.
+template <int WTM, int WTN, int WGM, int WGN, bool BF16, int KPS_ = kK16>
 struct Mfma16Tile {
-    static constexpr int BM = 64 * WTM, BN = 64 * WTN;
-    static constexpr int KPS = 64, EPW = 2, A_STEP = KPS / EPW, B_STEP = KPS;
-    using LA = Layout<BM, A_STEP, SwzA16>;     // BM rows x 32 words
-    using LB = Layout<KPS, BN / EPW, SwzB16>;  // 64 k rows x BN/2 words
+    static constexpr int BM = 32 * WTM * WGM, BN = 32 * WTN * WGN, WAVES = WGM * WGN;
+    static constexpr int KPS = KPS_, EPW = 2, A_STEP = KPS / EPW, B_STEP = KPS;
+    using LA = Layout<BM, A_STEP, typename std::conditional<KPS == 64, SwzA16, SwzA>::type>; // BM rows x KPS/2 words
+    using LB = Layout<KPS, BN / EPW, SwzB16>;                                                 // KPS k rows x BN/2 words
     f32x16 acc[WTM][WTN];
     int wm, wn, lane;
 
     __device__ void init(int tid) {
         lane = tid & 63;
         const int w = tid >> 6;
-        wm = w >> 1;
-        wn = w & 1;
+        wm = w / WGN;
+        wn = w % WGN;
 #pragma unroll
         for (int a = 0; a < WTM; ++a)
 #pragma unroll
@@ -364,6 +378,108 @@ struct Mfma16Tile {
                      : "v"(a0), "v"(a1), "i"(OFF0), "i"(OFF1));
     }
 
+#ifndef MGEMM_H16_PIPE
+#define MGEMM_H16_PIPE 1
+#endif
+    // One k step's operands: WTM A rows (16 bytes each) and two transposing
+    // B reads per column tile.
+    struct Frag {
+        u32x4 a[WTM];
+        i16x4 b[WTN][2];
+    };
+    // Issue one k step's LDS reads without waiting for them. `aa` addresses
+    // A row 32 WTM wm + l32 at this k step (row tiles ta are 32 rows, an
+    // immediate, apart: the swizzle repeats every 32 rows); ab[tb] address
+    // the B pieces; the k step's rows are immediates on top.
+    template <int KS>
+    __device__ static void issue_reads(unsigned aa, const unsigned *ab, Frag &f) {
+        constexpr int TA = 32 * LA::CPR * 16;
+        constexpr int B0 = (16 * KS) * LB::CPR * 16, B1 = (16 * KS + 4) * LB::CPR * 16;
+        if constexpr (WTM == 4)
+            asm volatile("ds_read_b128 %0, %8\n\t"
+                         "ds_read_b128 %1, %8 offset:%11\n\t"
+                         "ds_read_b128 %2, %8 offset:%12\n\t"
+                         "ds_read_b128 %3, %8 offset:%13\n\t"
+                         "ds_read_b64_tr_b16 %4, %9 offset:%14\n\t"
+                         "ds_read_b64_tr_b16 %5, %9 offset:%15\n\t"
+                         "ds_read_b64_tr_b16 %6, %10 offset:%14\n\t"
+                         "ds_read_b64_tr_b16 %7, %10 offset:%15"
+                         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]), "=&v"(f.b[0][0]),
+                           "=&v"(f.b[0][1]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1])
+                         : "v"(aa), "v"(ab[0]), "v"(ab[1]), "i"(TA), "i"(2 * TA), "i"(3 * TA), "i"(B0), "i"(B1));
+        else
+            asm volatile("ds_read_b128 %0, %6\n\t"
+                         "ds_read_b128 %1, %6 offset:%9\n\t"
+                         "ds_read_b64_tr_b16 %2, %7 offset:%10\n\t"
+                         "ds_read_b64_tr_b16 %3, %7 offset:%11\n\t"
+                         "ds_read_b64_tr_b16 %4, %8 offset:%10\n\t"
+                         "ds_read_b64_tr_b16 %5, %8 offset:%11"
+                         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]), "=&v"(f.b[1][0]),
+                           "=&v"(f.b[1][1])
+                         : "v"(aa), "v"(ab[0]), "v"(ab[1]), "i"(TA), "i"(B0), "i"(B1));
+    }
+    // Wait for every LDS read of this wave; the fragment's registers are
+    // outputs of the wait, so nothing reads them before it.
+    __device__ static void wait_reads(Frag &f) {
+        if constexpr (WTM == 4)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0][0]), "+v"(f.b[0][1]),
+                           "+v"(f.b[1][0]), "+v"(f.b[1][1]));
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.b[0][0]), "+v"(f.b[0][1]), "+v"(f.b[1][0]),
+                           "+v"(f.b[1][1]));
+    }
+    __device__ void mfma(const Frag &f) {
+#pragma unroll
+        for (int ta = 0; ta < WTM; ++ta)
+#pragma unroll
+            for (int tb = 0; tb < WTN; ++tb) {
+                const i16x4 lo = f.b[tb][0], hi = f.b[tb][1];
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                const i16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                if constexpr (BF16)
+                    acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, f.a[ta]), __builtin_bit_cast(bf16x8, bv), acc[ta][tb], 0, 0, 0);
+                else
+                    acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(f16x8, f.a[ta]), __builtin_bit_cast(f16x8, bv), acc[ta][tb], 0, 0, 0);
+            }
+    }
+
+#if MGEMM_H16_PIPE
+    // The k steps of a slice are software-pipelined: step ks+1's reads are
+    // in flight while step ks's MFMAs run (scheduling barriers keep the
+    // MFMAs between the issue and the wait).
+    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
+        static_assert(WTN == 2 && (WTM == 2 || WTM == 4), "issue_reads covers these wave tiles");
+        const int h = lane >> 5, l32 = lane & 31, q = lane & 15, g16 = (lane >> 4) & 1;
+        const unsigned as = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)As;
+        const unsigned bs = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)Bs;
+        const int m = 32 * WTM * wm + l32;
+        unsigned ab[WTN];
+#pragma unroll
+        for (int tb = 0; tb < WTN; ++tb) {
+            const int k = 8 * h + (q >> 2);
+            const int n = 32 * WTN * wn + 32 * tb + 16 * g16 + 4 * (q & 3);
+            ab[tb] = bs + LB::pos(k, n >> 3) * 16 + (n & 7) * 2;
+        }
+        constexpr int NKS = KPS / 16;
+        Frag f[2];
+        issue_reads<0>(as + LA::pos(m, h) * 16, ab, f[0]);
+        wait_reads(f[0]);
+        static_for<0, NKS>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
+            if constexpr (ks + 1 < NKS)
+                issue_reads<ks + 1>(as + LA::pos(m, 2 * (ks + 1) + h) * 16, ab, f[(ks + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(f[ks & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ks + 1 < NKS)
+                wait_reads(f[(ks + 1) & 1]);
+        });
+    }
+#else
     __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
         static_assert(WTN == 2, "read_b covers two 32-column tiles");
         const int h = lane >> 5, l32 = lane & 31, q = lane & 15, g16 = (lane >> 4) & 1;
@@ -406,6 +522,7 @@ struct Mfma16Tile {
                 }
         });
     }
+#endif
 
     __device__ void store(float *C, int ldc, int m0, int n0, int M, int N, bool) const {
         const int h = lane >> 5, l32 = lane & 31;
@@ -449,13 +566,18 @@ struct CfgMfma256x128 {
 };
 template <bool BF16>
 struct CfgH128 {
-    using Tile = Mfma16Tile<2, 2, BF16>;
+    using Tile = Mfma16Tile<2, 2, 2, 2, BF16>;
     static constexpr int BM = 128, BN = 128;
 };
 template <bool BF16>
 struct CfgH256x128 {
-    using Tile = Mfma16Tile<4, 2, BF16>;
+    using Tile = Mfma16Tile<4, 2, 2, 2, BF16>;
     static constexpr int BM = 256, BN = 128;
+};
+template <bool BF16>
+struct CfgH256x256 { // 8 waves (2 per SIMD), each 128 x 64 as in the 256 x 128 tile
+    using Tile = Mfma16Tile<4, 2, 2, 4, BF16>;
+    static constexpr int BM = 256, BN = 256;
 };
 
 // ---- block -> C tile ----------------------------------------------------------
@@ -521,8 +643,8 @@ template <class Tile, int W>
 struct GemmCtx {
     using LA = typename Tile::LA;
     using LB = typename Tile::LB;
-    using OA = Operand<LA, W>;
-    using OB = Operand<LB, W>;
+    using OA = Operand<LA, W, Tile::WAVES>;
+    using OB = Operand<LB, W, Tile::WAVES>;
     static constexpr int SLOT = LA::BYTES + LB::BYTES;
 
     OA oa;
@@ -612,10 +734,14 @@ struct SyncOps : GemmCtx<Tile, W> {
 };
 
 template <class Cfg, int S, bool PIPED, int W>
-__global__ void __launch_bounds__(kThreads) sgemm_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(64 * Cfg::Tile::WAVES) sgemm_kernel(GemmArgs g) {
     using Tile = typename Cfg::Tile;
     using Ctx = GemmCtx<Tile, W>;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[S * Ctx::SLOT];
+    // a ring deeper than the CU's LDS is never planned; its kernel is empty
+    constexpr bool kFits = S * Ctx::SLOT <= kLdsBytes;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kFits ? S * Ctx::SLOT : 1024];
+    if constexpr (!kFits)
+        return;
 
     int tm, tn;
     block_tile(blockIdx.x, g.gm, g.gn, tm, tn);

@@ -24,6 +24,7 @@ namespace {
 constexpr int64_t kMaxLd = int64_t(1) << 21;     // 256 rows x 2^21 words x 4 B: in-block byte offsets stay below 2^31
 constexpr int64_t kMaxExtent = int64_t(1) << 31; // rows * ld per operand, in elements
 constexpr int64_t kAutoBigTileBlocks = 512;      // 128x128 tiles once they give >= 2 blocks per CU
+constexpr int kMaxStages16 = 4;                  // asynchronous ring depth of the 16-bit GEMM
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -166,11 +167,15 @@ MG_GEMM_CFG(CfgMfma256x128)
     template __global__ void mgemm::sgemm_kernel<mgemm::CFG, S, false, W>(mgemm::GemmArgs);
 #define MG_GEMM16_CFG(CFG)                                                                               \
     MG_GEMM16_INST(CFG, 1, 16) MG_GEMM16_INST(CFG, 2, 16) MG_GEMM16_INST(CFG, 3, 16)                     \
-    MG_GEMM16_INST(CFG, 1, 4) MG_GEMM16_INST(CFG, 2, 4) MG_GEMM16_INST(CFG, 3, 4)
+    MG_GEMM16_INST(CFG, 1, 4) MG_GEMM16_INST(CFG, 2, 4) MG_GEMM16_INST(CFG, 3, 4)                        \
+    template __global__ void mgemm::sgemm_kernel<mgemm::CFG, 4, true, 16>(mgemm::GemmArgs);              \
+    template __global__ void mgemm::sgemm_kernel<mgemm::CFG, 4, true, 4>(mgemm::GemmArgs);
 MG_GEMM16_CFG(CfgH128<true>)
 MG_GEMM16_CFG(CfgH128<false>)
 MG_GEMM16_CFG(CfgH256x128<true>)
 MG_GEMM16_CFG(CfgH256x128<false>)
+MG_GEMM16_CFG(CfgH256x256<true>)
+MG_GEMM16_CFG(CfgH256x256<false>)
 #define MG_COPY_INST(S)                                                                                  \
     template __global__ void mgemm::tile_copy_kernel<S, 16, true>(mgemm::CopyArgs);                      \
     template __global__ void mgemm::tile_copy_kernel<S, 16, false>(mgemm::CopyArgs);                     \
@@ -249,8 +254,10 @@ int launch(const void *fn, int blocks, void *arg, hipStream_t stream, int thread
 int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                 const float *C, int64_t ldc, int dtype, int stages, int fill, int tile, mgemm_plan_t *pl) {
     if (M < 0 || N < 0 || K < 0 || (dtype != MGEMM_DTYPE_BF16 && dtype != MGEMM_DTYPE_F16) || stages < 1 ||
-        stages > kMaxSyncStages || (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED) ||
-        (tile != MGEMM_TILE_AUTO && tile != MGEMM_TILE_128x128 && tile != MGEMM_TILE_256x128))
+        stages > (fill == MGEMM_FILL_PIPED ? kMaxStages16 : kMaxSyncStages) ||
+        (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED) ||
+        (tile != MGEMM_TILE_AUTO && tile != MGEMM_TILE_128x128 && tile != MGEMM_TILE_256x128 &&
+         tile != MGEMM_TILE_256x256))
         return MGEMM_ERR_ARG;
     // the loaders move 32-bit words: pairs of 16-bit elements along k (A) and n (B)
     // (an empty operand is never read: its base and leading dimension are free)
@@ -272,9 +279,13 @@ int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
     const bool b128_ok = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 && N % 8 == 0;
     const int W = b128_ok ? 16 : 4;
     if (tile == MGEMM_TILE_AUTO)
-        tile = ((M + 255) / 256) * ((N + 127) / 128) >= 1024 ? MGEMM_TILE_256x128 : MGEMM_TILE_128x128;
-    const int bm = tile == MGEMM_TILE_256x128 ? 256 : 128, bn = 128;
-    constexpr int kps = 64;
+        // the largest tile that still gives every CU a block (measured at 4096^3 and 8192^3)
+        tile = ((M + 255) / 256) * ((N + 255) / 256) >= 256   ? MGEMM_TILE_256x256
+               : ((M + 255) / 256) * ((N + 127) / 128) >= 512 ? MGEMM_TILE_256x128
+                                                                : MGEMM_TILE_128x128;
+    const int bm = tile == MGEMM_TILE_128x128 ? 128 : 256, bn = tile == MGEMM_TILE_256x256 ? 256 : 128;
+    const int waves = tile == MGEMM_TILE_256x256 ? 8 : kWaves;
+    constexpr int kps = kK16;
     mgemm_plan_t p;
     std::memset(&p, 0, sizeof p);
     p.compute = MGEMM_COMPUTE_MFMA;
@@ -282,7 +293,7 @@ int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
     p.bm = bm;
     p.bn = bn;
     p.bk = kps;
-    p.threads = kThreads;
+    p.threads = 64 * waves;
     p.blocks = (int)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
     p.load_bytes = W;
     p.slices = (int)((K + kps - 1) / kps);
@@ -290,8 +301,10 @@ int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
     p.fill_mode = fill;
     const int slice_bytes = (bm * kps + kps * bn) * 2;
     p.lds_bytes = stages * slice_bytes;
-    p.loads_per_slice = slice_bytes / (64 * W) / kWaves;
+    p.loads_per_slice = slice_bytes / (64 * W) / waves;
     p.max_vmcnt = fill == MGEMM_FILL_PIPED ? std::min(63, std::max(0, stages - 2) * p.loads_per_slice) : 0;
+    if (p.lds_bytes > kLdsBytes)
+        return MGEMM_ERR_UNSUPPORTED;
     if (pl)
         *pl = p;
     return MGEMM_OK;
@@ -307,11 +320,19 @@ const void *gemm16_kernel_w(int S, int fill) {
     switch (S) {
     case 1: return gk16<Cfg, 1, W>(fill);
     case 2: return gk16<Cfg, 2, W>(fill);
-    default: return gk16<Cfg, 3, W>(fill);
+    case 3: return gk16<Cfg, 3, W>(fill);
+    default: return (const void *)&sgemm_kernel<Cfg, 4, true, W>; // piped only
     }
+}
+template <class Cfg>
+const void *gemm16_kernel(const mgemm_plan_t &p) {
+    return p.load_bytes == 16 ? gemm16_kernel_w<Cfg, 16>(p.stages, p.fill_mode)
+                              : gemm16_kernel_w<Cfg, 4>(p.stages, p.fill_mode);
 }
 const void *select_gemm16(const mgemm_plan_t &p, int dtype) {
     const bool big = p.tile == MGEMM_TILE_256x128, w16 = p.load_bytes == 16;
+    if (p.tile == MGEMM_TILE_256x256)
+        return dtype == MGEMM_DTYPE_BF16 ? gemm16_kernel<CfgH256x256<true>>(p) : gemm16_kernel<CfgH256x256<false>>(p);
     if (dtype == MGEMM_DTYPE_BF16) {
         if (big)
             return w16 ? gemm16_kernel_w<CfgH256x128<true>, 16>(p.stages, p.fill_mode)

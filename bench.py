@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "FP32 GEMM GFLOP/s + % FP32 peak at 4096³/8192³; piped/sync speedup; copy GB/s"
 PEAK_FP32_TFLOPS = 157.3   # MI355X dense FP32 (MFMA and packed vector), AMD spec
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, AMD spec
+PEAK_16BIT_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA (no sparsity), AMD spec
 # The 1 GiB fp32 array in 64x64 tiles, read two ways: as a 16384 x 16384
 # matrix (each tile row is 256 contiguous bytes, rows 64 KiB apart) and as a
 # 4194304 x 64 matrix (each tile is 16 KiB of contiguous memory).
@@ -274,6 +275,7 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
             del A, B, C
     res["gemm"] = gemm
     res["stage_study"] = stage_study(m, torch, Ad8, Bd8, Cd8)
+    res["gemm16"] = gemm16_table(m, datagen, torch, sorted({min(4096, big), big}))
     # tile copy: 1 GiB fp32 ~ N(0,1), 64x64 tiles, 2 x bytes moved
     n_el = 1 << 28
     src = datagen.normal01_torch(datagen.SEED_COPY, n_el, device="cuda")
@@ -295,6 +297,49 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
     res["tile_copy_1GiB"] = copy
     del src, dst
     return res
+
+
+GEMM16_VARIANTS = (("128x128", "sync", 1), ("128x128", "piped", 2), ("256x128", "sync", 1), ("256x128", "piped", 1),
+                   ("256x128", "piped", 2), ("256x128", "piped", 3), ("256x256", "sync", 1), ("256x256", "sync", 2),
+                   ("256x256", "piped", 1), ("256x256", "piped", 2))
+
+
+def gemm16_table(m, datagen, torch, sizes):
+    """bfloat16 / binary16 inputs, fp32 accumulation and output
+    (mgemm_gemm16): TFLOP/s and share of the 2.5 PFLOP/s dense 16-bit MFMA
+    peak per tile, fill and ring depth, after a bitwise piped == sync gate on
+    the whole output; torch.matmul (16-bit output) as context."""
+    out = {}
+    for fmt in ("bf16", "f16"):
+        for n in sizes:
+            A = datagen.grid16_torch(datagen.SEED_A, n, n, fmt, device="cuda")
+            B = datagen.grid16_torch(datagen.SEED_B, n, n, fmt, device="cuda")
+            C = torch.empty((n, n), device="cuda")
+            C1 = torch.empty((n, n), device="cuda")
+            flop = 2.0 * n ** 3
+            row = {}
+            for tile, fill, S in GEMM16_VARIANTS:
+                try:
+                    m.plan16(n, n, n, dtype=fmt, stages=S, fill=fill, tile=tile)
+                except m.MgemmError:
+                    continue
+                m.gemm16(A, B, C, stages=S, fill=fill, tile=tile)
+                m.gemm16(A, B, C1, stages=1, fill="sync", tile=tile)
+                torch.cuda.synchronize()
+                if not torch.equal(C.view(torch.int32), C1.view(torch.int32)):
+                    raise SystemExit(f"gemm16 parity gate: {fmt} {n} {tile} {fill} S{S} differs from sync S1")
+                t = timed_launches(lambda: m.gemm16(A, B, C, stages=S, fill=fill, tile=tile), repeats=3)
+                tf = flop / (t["ms_median"] * 1e-3) / 1e12
+                row[f"{tile}_{fill}_S{S}"] = {"ms": round(t["ms_median"], 4), "tflops": round(tf, 1),
+                                              "pct_peak": round(100 * tf / PEAK_16BIT_TFLOPS, 2)}
+            t = timed_launches(lambda: torch.matmul(A, B), repeats=3)
+            row["torch_matmul_context"] = {"ms": round(t["ms_median"], 4),
+                                           "tflops": round(flop / (t["ms_median"] * 1e-3) / 1e12, 1)}
+            best = max((k for k in row if k != "torch_matmul_context"), key=lambda k: row[k]["tflops"])
+            row["best"] = best
+            out[f"{fmt}_{n}"] = row
+            del A, B, C, C1
+    return out
 
 
 def stage_study(m, torch, Ad8, Bd8, Cd8):

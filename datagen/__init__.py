@@ -188,6 +188,23 @@ def grid_pm1(seed: int, n: int, bits: int) -> np.ndarray:
     return _fill(n, part)
 
 
+def grid16_torch(seed: int, rows: int, cols: int, fmt: str, device="cpu"):
+    """rows x cols torch bfloat16 / float16 tensor holding the values of
+    grid_pm1(seed, rows * cols, bits) (the "grid" kind of matrix16, no
+    padding), produced by torch on ``device``."""
+    import torch
+    bits = 8 if fmt == "bf16" else 11
+    n = rows * cols
+    out = torch.empty(n, dtype=torch.bfloat16 if fmt == "bf16" else torch.float16, device=device)
+    step = 1 << 24
+    for s in range(0, n, step):
+        c = min(step, n - s)
+        z, lsr = _torch_words(seed, s, c, device)
+        top = lsr(z, 64 - bits)
+        out[s:s + c] = ((top - (1 << (bits - 1))).to(torch.float64) * 2.0 ** -(bits - 1)).to(out.dtype)
+    return out.view(rows, cols)
+
+
 def to_bits16(x: np.ndarray, fmt: str) -> np.ndarray:
     """uint16 bit patterns of fp32 values that the format represents exactly
     ("bf16": upper half of the binary32 pattern; "f16": IEEE binary16)."""

@@ -62,6 +62,7 @@ struct mgemm_plan; /* defined below (mgemm_plan_t) */
 #define MGEMM_TILE_64x64 1   /* VALU: 4x4 micro-tile per thread (the pages' shape) */
 #define MGEMM_TILE_128x128 2 /* VALU: 8x8 micro-tile; MFMA: 2x2 32x32 tiles per wave */
 #define MGEMM_TILE_256x128 3 /* MFMA only: 4x2 32x32 tiles per wave (BM 256, BN 128) */
+#define MGEMM_TILE_256x256 4 /* 16-bit only: 8 waves of 4x2 32x32 tiles (BM 256, BN 256) */
 
 /* loader: width of each lane's global load (results never depend on it). */
 #define MGEMM_LOADER_AUTO 0 /* 16 B when bases, ld and extents allow, else 4 B */
@@ -115,9 +116,11 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K,
  * same asynchronous LDS ring (64-element K slices). Products and sums are
  * fp32 inside the MFMA. lda and ldb count 16-bit elements, ldc fp32
  * elements. Requirements (else MGEMM_ERR_ARG): K, N, lda and ldb even; A and
- * B 4-byte aligned. stages 1 .. 3; fill_mode MGEMM_FILL_SYNC or
+ * B 4-byte aligned. stages 1 .. 4 (piped) or 1 .. 3 (sync); fill_mode MGEMM_FILL_SYNC or
  * MGEMM_FILL_PIPED (bit-identical results); tile MGEMM_TILE_AUTO,
- * MGEMM_TILE_128x128 or MGEMM_TILE_256x128. Other conventions as mgemm_sgemm.
+ * MGEMM_TILE_128x128, MGEMM_TILE_256x128 or MGEMM_TILE_256x256 (512 threads); a
+ * ring deeper than the CU's 160 KiB of LDS gives MGEMM_ERR_UNSUPPORTED.
+ * Other conventions as mgemm_sgemm.
  */
 int mgemm_gemm16(int64_t M, int64_t N, int64_t K,
                  const void *A, int64_t lda,

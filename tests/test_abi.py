@@ -453,14 +453,16 @@ def g16(M=64, N=64, K=64, A=A0, lda=None, B=B0, ldb=None, C=C0, ldc=None, dtype=
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(dtype=0), m.ERR_ARG), (dict(dtype=3), m.ERR_ARG), (dict(stages=0), m.ERR_ARG), (dict(stages=4), m.ERR_ARG),
-    (dict(fill=2), m.ERR_ARG), (dict(tile=1), m.ERR_ARG), (dict(tile=4), m.ERR_ARG),
+    (dict(dtype=0), m.ERR_ARG), (dict(dtype=3), m.ERR_ARG), (dict(stages=0), m.ERR_ARG), (dict(stages=5), m.ERR_ARG),
+    (dict(stages=4, fill=0), m.ERR_ARG),
+    (dict(fill=2), m.ERR_ARG), (dict(tile=1), m.ERR_ARG), (dict(tile=5), m.ERR_ARG),
     (dict(K=63, lda=64), m.ERR_ARG), (dict(N=63, ldb=64, ldc=64), m.ERR_ARG), (dict(lda=65), m.ERR_ARG),
     (dict(ldb=65), m.ERR_ARG), (dict(A=A0 + 2), m.ERR_ARG), (dict(B=B0 + 6), m.ERR_ARG), (dict(lda=62), m.ERR_ARG),
     (dict(ldc=63), m.ERR_ARG), (dict(A=0), m.ERR_ARG), (dict(C=0), m.ERR_ARG),
     (dict(C=A0), m.ERR_ALIAS), (dict(C=B0 + 2 * 64 * 63), m.ERR_ALIAS), (dict(C=A0 + 2 * 64 * 64), m.OK),
     (dict(lda=1 << 22), m.ERR_UNSUPPORTED),
     (dict(A=A0 + 4), m.OK), (dict(B=B0 + 4, ldb=66), m.OK), (dict(stages=3, fill=0, tile=3), m.OK),
+    (dict(tile=4), m.OK),
 ])
 def test_gemm16_validation(kw, want):
     assert g16(**kw) == want
@@ -481,12 +483,24 @@ def test_gemm16_empty_operands_ignore_layout():
 
 
 def test_gemm16_plans():
+    bk = m.plan16(64, 64, 64)["bk"]
+    assert bk in (32, 64)
     p = m.plan16(8192, 8192, 8192)
+    assert (p["bm"], p["bn"], p["threads"], p["blocks"]) == (256, 256, 512, 32 * 32)
+    assert m.plan16(4096, 4096, 4096)["bn"] == 256 and m.plan16(4096, 2048, 64)["bn"] == 128
+    assert m.plan16(2048, 2048, 2048)["bm"] == 128
+    assert p["lds_bytes"] == 2 * (256 + 256) * bk * 2 and p["loads_per_slice"] == (256 + 256) * bk * 2 // 1024 // 8
+    # rings beyond the 160 KiB of LDS are refused
+    st, _ = m.mgemm_plan_gemm16(8192, 8192, 8192, A0, 8192, B0, 8192, C0, 8192, 1, 3, 1, 4)
+    assert st == (m.ERR_UNSUPPORTED if 3 * (256 + 256) * bk * 2 > 160 * 1024 else m.OK)
+    if bk != 64:
+        return
+    p = m.plan16(8192, 8192, 8192, tile="256x128")
     assert (p["bm"], p["bn"], p["bk"], p["blocks"], p["load_bytes"]) == (256, 128, 64, 32 * 64, 16)
     assert p["slices"] == 128 and p["lds_bytes"] == 2 * (256 + 128) * 64 * 2 and p["compute"] == m.COMPUTE_MFMA
     # one slice: (256 x 64 + 64 x 128) 16-bit elements = 48 KiB = 12 dwordx4 per lane of each of 4 waves
     assert p["loads_per_slice"] == 12 and p["max_vmcnt"] == 0
-    assert m.plan16(8192, 8192, 8192, stages=3)["max_vmcnt"] == 12
+    assert m.plan16(8192, 8192, 8192, stages=3, tile="256x128")["max_vmcnt"] == 12
     assert m.plan16(8192, 8192, 8192, stages=3, tile="256x128")["lds_bytes"] == 3 * 49152 <= 160 * 1024
     p = m.plan16(1024, 1024, 1024, dtype="f16")
     assert (p["bm"], p["blocks"]) == (128, 64)
@@ -501,17 +515,30 @@ def _name16(cfg, bf16, S, piped, W):
     return f"_ZN5mgemm12sgemm_kernelINS_{len(cfg)}{cfg}ILb{int(bf16)}EEELi{S}ELb{int(piped)}ELi{W}EEEvNS_8GemmArgsE"
 
 
-@pytest.mark.parametrize("cfg", ["CfgH128", "CfgH256x128"])
+H16_CFGS = ["CfgH128", "CfgH256x128", "CfgH256x256"]
+H16_TILE = {"CfgH128": "128x128", "CfgH256x128": "256x128", "CfgH256x256": "256x256"}
+
+
+def _fits16(cfg, S):
+    st, _ = m.mgemm_plan_gemm16(1024, 1024, 1024, A0, 1024, B0, 1024, C0, 1024, 1, S, 1,
+                                {"CfgH128": 2, "CfgH256x128": 3, "CfgH256x256": 4}[cfg])
+    return st == m.OK
+
+
+@pytest.mark.parametrize("cfg", H16_CFGS)
 @pytest.mark.parametrize("bf16", [True, False])
 def test_isa_gemm16(isa, cfg, bf16):
     """The 16-bit kernels multiply on v_mfma_f32_32x32x16_{bf16,f16}, read B
     through the transposing LDS read, fill LDS asynchronously (piped) or
     through VGPRs (sync), and never drain the prefetch before the MFMAs."""
     mfma = "v_mfma_f32_32x32x16_" + ("bf16" if bf16 else "f16")
-    per_slice = {"CfgH128": 4 * 4, "CfgH256x128": 8 * 4}[cfg]  # WTM*WTN tiles x 4 k-steps per slice
-    for S in (1, 2, 3):
+    bk = m.plan16(64, 64, 64)["bk"]
+    per_slice = {"CfgH128": 4, "CfgH256x128": 8, "CfgH256x256": 8}[cfg] * bk // 16  # WTM*WTN x k steps
+    for S in (1, 2, 3, 4):
+        if not _fits16(cfg, S):
+            continue
         for W in (16, 4):
-            for piped in (True, False):
+            for piped in ((True, False) if S < 4 else (True,)):
                 lines = isa[_name16(cfg, bf16, S, piped, W)]
                 body = "\n".join(lines)
                 assert body.count(mfma) >= per_slice, (cfg, S, W, piped)
@@ -526,3 +553,52 @@ def test_isa_gemm16(isa, cfg, bf16):
                 else:
                     assert "ds_write" in body and not re.search(r"buffer_load\S* .* lds", body)
                 assert "v_pk_fma_f32" not in body and "v_pk_add_f32" not in body and "v_pk_mul_f32" not in body
+
+
+def _regs(operand):
+    """VGPR indices named by one operand ('v7', 'v[30:33]'), else empty."""
+    mm = re.fullmatch(r"v(\d+)", operand) or re.fullmatch(r"v\[(\d+):(\d+)\]", operand)
+    if not mm:
+        return set()
+    lo = int(mm.group(1))
+    hi = int(mm.group(2)) if mm.lastindex == 2 else lo
+    return set(range(lo, hi + 1))
+
+
+def _early_uses_of_lds_results(lines):
+    """Instructions that read or overwrite the destination of an LDS read
+    before an s_waitcnt lgkmcnt(0) (in layout order): the wait the LDS
+    reads issued from inline asm depend on."""
+    pending, bad = set(), []
+    for raw in lines:
+        ins = raw.split(";")[0].strip()
+        if not ins or ins.startswith(".") or ins.endswith(":"):
+            continue
+        op, _, rest = ins.partition(" ")
+        ops = [o.strip() for o in rest.split(",")]
+        if op == "s_waitcnt" and "lgkmcnt(0)" in rest:
+            pending.clear()
+            continue
+        used = set().union(*(_regs(o.split()[0]) for o in ops if o)) if ops else set()
+        if used & pending:
+            bad.append(ins)
+        if op.startswith("ds_read"):
+            pending |= _regs(ops[0])
+    return bad
+
+
+def test_isa_guard_sees_an_early_use():
+    lines = ["ds_read_b128 v[4:7], v1", "v_mov_b32_e32 v9, v5", "s_waitcnt lgkmcnt(0)", "v_mov_b32_e32 v9, v5"]
+    assert _early_uses_of_lds_results(lines) == ["v_mov_b32_e32 v9, v5"]
+    assert _early_uses_of_lds_results(lines[:1] + lines[2:]) == []
+
+
+@pytest.mark.parametrize("cfg", H16_CFGS)
+def test_isa_gemm16_reads_are_waited_for(isa, cfg):
+    """No instruction touches an LDS read's destination before the wait."""
+    for bf16 in (True, False):
+        for S in (1, 2, 3):
+            for W in (16, 4):
+                for piped in (True, False):
+                    bad = _early_uses_of_lds_results(isa[_name16(cfg, bf16, S, piped, W)])
+                    assert not bad, (cfg, bf16, S, W, piped, bad[:3])

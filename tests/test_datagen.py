@@ -55,3 +55,12 @@ def test_matrix_padding():
     m = datagen.matrix("uniform", 1, 3, 5, ld=8)
     assert m.shape == (3, 8) and np.all(np.isnan(m[:, 5:]))
     assert np.array_equal(m[:, :5].ravel(), datagen.uniform_pm1(1, 15))
+
+
+def test_torch_twin_of_the_16bit_grid_matches():
+    import torch
+    for fmt, dt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        want = datagen.matrix16(9, 33, 515, fmt)
+        got = datagen.grid16_torch(9, 33, 515, fmt)
+        assert got.dtype == dt and got.shape == (33, 515)
+        assert np.array_equal(got.view(torch.int16).numpy().view(np.uint16), want), fmt

@@ -28,6 +28,16 @@ def dev16(bits: np.ndarray, fmt: str, ld: int | None = None, offset: int = 0, ex
     return t[offset:offset + rows * ld].view(rows, ld)[:, :cols]
 
 
+TILES16 = ("128x128", "256x128", "256x256")
+
+
+def fits(tile, S):
+    """The ring of this tile and depth fits the CU's LDS."""
+    st, _ = m.mgemm_plan_gemm16(1024, 1024, 1024, 1 << 32, 1024, 1 << 36, 1024, 1 << 40, 1024, m.DTYPE_BF16, S,
+                                m.FILL_PIPED, m._TILE[tile])
+    return st == m.OK
+
+
 def check16(C, A, B, fmt, rows=None, what=""):
     if rows is not None:
         A = np.ascontiguousarray(A[rows])
@@ -60,10 +70,12 @@ def test_every_variant(fmt, layout):
     W = m.plan16(M, N, K, dtype=fmt, lda=lda, ldb=ldb, ldc=ldc, a_ptr=Ad.data_ptr(), b_ptr=Bd.data_ptr(),
                  c_ptr=out_device(M, N, ldc, offset=oc).data_ptr())["load_bytes"]
     assert W == (16 if layout in ("aligned", "ragged_b128") else 4)
-    for tile in ("128x128", "256x128"):
+    for tile in TILES16:
         ref = None
         for fill in ("sync", "piped"):
-            for S in (1, 2, 3):
+            for S in (1, 2, 3, 4):
+                if not fits(tile, S) or (fill == "sync" and S == 4):
+                    continue
                 Cd = out_device(M, N, ldc, offset=oc)
                 m.gemm16(Ad, Bd, Cd, stages=S, fill=fill, tile=tile)
                 torch.cuda.synchronize()
@@ -84,8 +96,10 @@ def test_coarse_grid_exact(fmt):
     B = datagen.matrix16(4, K, N, fmt, kind="coarse")
     want = oracle.gemm16_f64(A, B, fmt).astype(np.float32)
     Ad, Bd = dev16(A, fmt), dev16(B, fmt)
-    for tile in ("128x128", "256x128"):
-        for fill, S in (("sync", 1), ("piped", 2), ("piped", 3)):
+    for tile in TILES16:
+        for fill, S in (("sync", 1), ("piped", 2), ("piped", 3), ("piped", 4)):
+            if not fits(tile, S):
+                continue
             C = m.gemm16(Ad, Bd, stages=S, fill=fill, tile=tile)
             torch.cuda.synchronize()
             assert same_bits(C.cpu().numpy(), want), (fmt, tile, fill, S)
@@ -122,10 +136,12 @@ def test_full_size_8192(fmt):
     Ad, Bd = dev16(A, fmt, extra_rows=0), dev16(B, fmt, extra_rows=0)
     ref = m.gemm16(Ad, Bd, stages=2, fill="piped")
     other = torch.empty_like(ref)
-    for fill, S in (("sync", 1), ("piped", 3)):
-        m.gemm16(Ad, Bd, other, stages=S, fill=fill)
+    for fill, S, tile in (("sync", 1, "auto"), ("sync", 2, "auto"), ("piped", 3, "256x128"), ("piped", 1, "256x128"),
+                          ("sync", 1, "128x128")):
+        other.fill_(float("nan"))
+        m.gemm16(Ad, Bd, other, stages=S, fill=fill, tile=tile)
         torch.cuda.synchronize()
-        assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), (fmt, fill, S)
+        assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), (fmt, fill, S, tile)
     rows = np.unique(np.r_[0, 1, n // 2, n - 1, np.linspace(0, n - 1, 8).astype(int)])
     check16(ref[torch.as_tensor(rows, device="cuda")].cpu().numpy(), A[rows], B, fmt,
             what=f"{fmt} 8192^3 sampled rows")
