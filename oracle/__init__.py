@@ -1,4 +1,5 @@
-"""TEST INFRASTRUCTURE: the CPU oracle for the pipelined FP32 GEMM and tile copy.
+"""TEST INFRASTRUCTURE: the CPU oracle for the pipelined GEMMs (fp32 and 16-bit
+inputs), the tile copy and scaled dot-product attention.
 
 Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
 import this package. The product library never loads it, and it shares no code
@@ -59,6 +60,9 @@ def _bind(lib):
     lib.oracle_decode16.restype = ctypes.c_double
     lib.oracle_gemm16_f64.argtypes = [i64, i64, i64, fp, i64, fp, i64, dp, i64, ctypes.c_int, ctypes.c_int]
     lib.oracle_gemm16_f64.restype = None
+    lib.oracle_attention_f64.argtypes = [i64, i64, i64, i64, fp, i64, fp, i64, fp, i64, ctypes.c_double,
+                                         ctypes.c_int, dp, dp, i64]
+    lib.oracle_attention_f64.restype = ctypes.c_int
     return lib
 
 
@@ -152,3 +156,45 @@ def timed_gemm_rows(A: np.ndarray, B: np.ndarray, rows: int, lib=None):
     lib.oracle_gemm_f64(M, N, K, _ptr(A), A.strides[0] // 4, _ptr(B), B.strides[0] // 4, _ptr(C), N)
     dt = time.perf_counter() - t0
     return dt, 2.0 * M * N * K
+
+
+def attention_f64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, fmt: str, scale: float, with_abs: bool = False,
+                  lib=None):
+    """softmax(scale * Q K^T) V in fp64 for 16-bit patterns Q (..., Sq, D),
+    K (..., Sk, D), V (..., Sk, Dv) with any leading (batch, head) axes and
+    unit stride along the last axis; returns O (..., Sq, Dv) and, with
+    ``with_abs``, the weighted magnitudes sum_j w_j |v_jc| too."""
+    lib = lib or load()
+    for name, x in (("Q", Q), ("K", K), ("V", V)):
+        if x.dtype != np.uint16 or x.ndim < 2 or (x.size and x.strides[-1] != 2):
+            raise TypeError(f"{name} must hold uint16 patterns with unit stride along its last axis")
+    lead = Q.shape[:-2]
+    if K.shape[:-2] != lead or V.shape[:-2] != lead:
+        raise ValueError("Q, K and V need the same leading axes")
+    Sq, D = Q.shape[-2:]
+    Sk, Dv = V.shape[-2:]
+    if K.shape[-2:] != (Sk, D):
+        raise ValueError("K must be Sk x D")
+    if Sk < 1:
+        raise ValueError("softmax over an empty key set is undefined")
+    O = np.zeros(lead + (Sq, Dv))
+    W = np.zeros(lead + (Sq, Dv)) if with_abs else None
+    for idx in np.ndindex(*lead):
+        q, k, v = Q[idx], K[idx], V[idx]
+        o = O[idx]
+        w = W[idx] if with_abs else None
+        st = lib.oracle_attention_f64(Sq, Sk, D, Dv, _ptr(q), q.strides[0] // 2, _ptr(k), k.strides[0] // 2,
+                                      _ptr(v), v.strides[0] // 2, float(scale), FMT[fmt], _ptr(o),
+                                      _ptr(w) if with_abs else None, Dv)
+        if st != 0:
+            raise MemoryError("oracle_attention_f64: out of memory")
+    return (O, W) if with_abs else O
+
+
+def attention_bound(Wabs: np.ndarray, fmt: str) -> np.ndarray:
+    """Acceptance bound of the attention kernels: 2^-6 (bfloat16) or 2^-8
+    (binary16) times sum_j w_j |v_jc|. The probabilities are rounded to the
+    16-bit format before the P V product (unit roundoff 2^-8 or 2^-11), which
+    moves each weight by at most about twice that; fp32 accumulation and the
+    rescaling steps add far less for key counts below 2^14."""
+    return (2.0 ** -6 if fmt == "bf16" else 2.0 ** -8) * Wabs

@@ -1,8 +1,9 @@
 /*
  * oracle/ref_gemm.c -- TEST INFRASTRUCTURE, not part of the product path.
  *
- * A plain, slow, obviously correct CPU reference for what the pipelined FP32
- * GEMM and the pipelined tile copy compute. Only the test suite, the smoke
+ * A plain, slow, obviously correct CPU reference for what the pipelined GEMMs
+ * (fp32, and bfloat16 / binary16 inputs), the pipelined tile copy and the
+ * pipelined attention compute. Only the test suite, the smoke
  * check and the CPU-baseline leg of the benchmark load this library. It shares
  * no source, header, table or helper with the HIP library; the two meet only
  * through the seeded inputs of the datagen package.
@@ -28,6 +29,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -156,4 +158,71 @@ void oracle_gemm16_f64(int64_t M, int64_t N, int64_t K,
             }
         }
     }
+}
+
+/* ---- scaled dot-product attention over 16-bit Q, K, V --------------------
+ * "A study on CUDA async memcpy" (the FlashAttention tile pipeline section):
+ * Q tiles stay put while K/V tiles stream past them, each step scoring the
+ * current K tile, rescaling the running result and accumulating V. That
+ * online form reaches, up to rounding, the plain definition written here:
+ *   s_j   = scale * sum_{d<D} q_d * k_jd                        (j < Sk)
+ *   w_j   = exp(s_j - max_t s_t) / sum_u exp(s_u - max_t s_t)
+ *   O_c   = sum_j w_j * v_jc                                    (c < Dv)
+ * per query row q (i < Sq), all in fp64 from the decoded 16-bit inputs
+ * (subtracting the row maximum changes nothing mathematically; it keeps
+ * exp in range). Wabs_c = sum_j w_j * |v_jc| is the magnitude that scales
+ * the acceptance bound. Row-major Q (Sq x D, ldq), K (Sk x D, ldk),
+ * V (Sk x Dv, ldv), O and Wabs (Sq x Dv, ldo); Sk >= 1; Wabs may be NULL.
+ * Returns 0, or -1 if scratch memory cannot be allocated. */
+int oracle_attention_f64(int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
+                         const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk,
+                         const uint16_t *V, int64_t ldv, double scale, int fmt,
+                         double *O, double *Wabs, int64_t ldo)
+{
+    int failed = 0;
+    int64_t i;
+#pragma omp parallel for schedule(static) reduction(| : failed)
+    for (i = 0; i < Sq; ++i) {
+        double *s = (double *)malloc((size_t)(Sk > 0 ? Sk : 1) * sizeof(double));
+        double *q = (double *)malloc((size_t)(D > 0 ? D : 1) * sizeof(double));
+        int64_t j, d, c;
+        double mx = -INFINITY, sum = 0.0;
+        if (!s || !q) {
+            free(s);
+            free(q);
+            failed = 1;
+            continue;
+        }
+        for (d = 0; d < D; ++d)
+            q[d] = oracle_decode16(Q[i * ldq + d], fmt);
+        for (j = 0; j < Sk; ++j) {
+            double acc = 0.0;
+            for (d = 0; d < D; ++d)
+                acc += q[d] * oracle_decode16(K[j * ldk + d], fmt);
+            s[j] = scale * acc;
+            if (s[j] > mx)
+                mx = s[j];
+        }
+        for (j = 0; j < Sk; ++j) {
+            s[j] = exp(s[j] - mx);
+            sum += s[j];
+        }
+        for (c = 0; c < Dv; ++c) {
+            O[i * ldo + c] = 0.0;
+            if (Wabs)
+                Wabs[i * ldo + c] = 0.0;
+        }
+        for (j = 0; j < Sk; ++j) {
+            const double w = s[j] / sum;
+            for (c = 0; c < Dv; ++c) {
+                const double v = oracle_decode16(V[j * ldv + c], fmt);
+                O[i * ldo + c] += w * v;
+                if (Wabs)
+                    Wabs[i * ldo + c] += w * fabs(v);
+            }
+        }
+        free(s);
+        free(q);
+    }
+    return failed ? -1 : 0;
 }

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests import oracle16_pins, oracle_pins
+from tests import oracle16_pins, oracle_attn_pins, oracle_pins
 
 
 @pytest.fixture(scope="module")
@@ -16,7 +16,10 @@ def lib():
     return oracle.load()
 
 
-@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS + oracle16_pins.ALL_PINS16, ids=lambda f: f.__name__)
+ALL = list(oracle_pins.ALL_PINS) + list(oracle16_pins.ALL_PINS16) + list(oracle_attn_pins.ALL_ATTN_PINS)
+
+
+@pytest.mark.parametrize("pin", ALL, ids=lambda f: f.__name__)
 def test_pin(lib, pin):
     pin(lib)
 
@@ -44,6 +47,16 @@ MUTANTS = {
     "bf16_wrong_shift": ("v.u = (uint32_t)h << 16;", "v.u = (uint32_t)h << 15;"),
     "gemm16_abs_keeps_b_sign": ("c[j] += a * (absolute ? fabs(bv) : bv);", "c[j] += a * bv;"),
     "gemm16_drops_first_term": ("for (p = 0; p < K; ++p) {\n            double a = oracle_decode16", "for (p = 1; p < K; ++p) {\n            double a = oracle_decode16"),
+    "attn_drops_scale": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "attn_transposed_K": ("oracle_decode16(K[j * ldk + d], fmt)", "oracle_decode16(K[d * ldk + j], fmt)"),
+    "attn_no_max": ("s[j] = exp(s[j] - mx);", "s[j] = exp(s[j]);"),
+    "attn_max_of_first_key": ("if (s[j] > mx)", "if (j == 0)"),
+    "attn_unnormalised": ("const double w = s[j] / sum;", "const double w = s[j];"),
+    "attn_drops_last_key": ("for (j = 0; j < Sk; ++j) {\n            const double w", "for (j = 0; j < Sk - 1; ++j) {\n            const double w"),
+    "attn_abs_keeps_sign": ("Wabs[i * ldo + c] += w * fabs(v);", "Wabs[i * ldo + c] += w * v;"),
+    "attn_ignores_ldv": ("V[j * ldv + c]", "V[j * Dv + c]"),
+    "attn_ignores_ldq": ("Q[i * ldq + d]", "Q[i * D + d]"),
+    "attn_query_shift": ("q[d] = oracle_decode16(Q[i * ldq + d], fmt);", "q[d] = oracle_decode16(Q[((i + 1) % Sq) * ldq + d], fmt);"),
 }
 
 
@@ -61,7 +74,7 @@ def test_mutant_is_caught(name):
         subprocess.run(["gcc", *oracle.CFLAGS, path, "-o", so, "-lm"], check=True)
         lib = oracle.load(so)
         failed = []
-        for pin in oracle_pins.ALL_PINS + oracle16_pins.ALL_PINS16:
+        for pin in ALL:
             try:
                 pin(lib)
             except (AssertionError, ValueError, OverflowError):
