@@ -61,7 +61,7 @@ def _bind(lib):
     lib.oracle_gemm16_f64.argtypes = [i64, i64, i64, fp, i64, fp, i64, dp, i64, ctypes.c_int, ctypes.c_int]
     lib.oracle_gemm16_f64.restype = None
     lib.oracle_attention_f64.argtypes = [i64, i64, i64, i64, fp, i64, fp, i64, fp, i64, ctypes.c_double,
-                                         ctypes.c_int, dp, dp, i64]
+                                         ctypes.c_int, dp, dp, i64, dp]
     lib.oracle_attention_f64.restype = ctypes.c_int
     return lib
 
@@ -163,7 +163,8 @@ def attention_f64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, fmt: str, scale: 
     """softmax(scale * Q K^T) V in fp64 for 16-bit patterns Q (..., Sq, D),
     K (..., Sk, D), V (..., Sk, Dv) with any leading (batch, head) axes and
     unit stride along the last axis; returns O (..., Sq, Dv) and, with
-    ``with_abs``, the weighted magnitudes sum_j w_j |v_jc| too."""
+    ``with_abs``, (O, Wabs, G): the weighted magnitudes sum_j w_j |v_jc|
+    (..., Sq, Dv) and the score magnitudes max_j sum_d |q_d||k_jd| (..., Sq)."""
     lib = lib or load()
     for name, x in (("Q", Q), ("K", K), ("V", V)):
         if x.dtype != np.uint16 or x.ndim < 2 or (x.size and x.strides[-1] != 2):
@@ -179,22 +180,32 @@ def attention_f64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, fmt: str, scale: 
         raise ValueError("softmax over an empty key set is undefined")
     O = np.zeros(lead + (Sq, Dv))
     W = np.zeros(lead + (Sq, Dv)) if with_abs else None
+    G = np.zeros(lead + (Sq,)) if with_abs else None
     for idx in np.ndindex(*lead):
         q, k, v = Q[idx], K[idx], V[idx]
         o = O[idx]
         w = W[idx] if with_abs else None
+        g = G[idx] if with_abs else None
         st = lib.oracle_attention_f64(Sq, Sk, D, Dv, _ptr(q), q.strides[0] // 2, _ptr(k), k.strides[0] // 2,
                                       _ptr(v), v.strides[0] // 2, float(scale), FMT[fmt], _ptr(o),
-                                      _ptr(w) if with_abs else None, Dv)
+                                      _ptr(w) if with_abs else None, Dv, _ptr(g) if with_abs else None)
         if st != 0:
             raise MemoryError("oracle_attention_f64: out of memory")
-    return (O, W) if with_abs else O
+    return (O, W, G) if with_abs else O
 
 
-def attention_bound(Wabs: np.ndarray, fmt: str) -> np.ndarray:
-    """Acceptance bound of the attention kernels: 2^-6 (bfloat16) or 2^-8
-    (binary16) times sum_j w_j |v_jc|. The probabilities are rounded to the
-    16-bit format before the P V product (unit roundoff 2^-8 or 2^-11), which
-    moves each weight by at most about twice that; fp32 accumulation and the
-    rescaling steps add far less for key counts below 2^14."""
-    return (2.0 ** -6 if fmt == "bf16" else 2.0 ** -8) * Wabs
+def attention_bound(Wabs: np.ndarray, fmt: str, G: np.ndarray, scale: float, D: int) -> np.ndarray:
+    """Acceptance bound of the attention kernels, elementwise:
+    (e_p + 4 delta_i) * sum_j w_j |v_jc|. e_p = 2^-6 (bfloat16) or 2^-8
+    (binary16): the probabilities are rounded to the 16-bit format before the
+    P V product (unit roundoff 2^-8 or 2^-11), which moves each weight by at
+    most about twice that, with fp32 accumulation and rescaling adding far
+    less for key counts below 2^14. delta_i = |scale| (D + 8) 2^-24 G_i bounds
+    the error of every score of query row i (fp32 sums of D exact products,
+    then the fp32 scaling into the exponent and the shift by the row
+    maximum); perturbing every score by at most delta moves each softmax
+    weight by a factor within exp(+-2 delta), so O by at most
+    2 delta sum_j w_j |v_jc|, taken twice."""
+    e_p = 2.0 ** -6 if fmt == "bf16" else 2.0 ** -8
+    delta = abs(scale) * (D + 8) * 2.0 ** -24 * G
+    return (e_p + 4.0 * delta[..., None]) * Wabs

@@ -170,14 +170,16 @@ void oracle_gemm16_f64(int64_t M, int64_t N, int64_t K,
  *   O_c   = sum_j w_j * v_jc                                    (c < Dv)
  * per query row q (i < Sq), all in fp64 from the decoded 16-bit inputs
  * (subtracting the row maximum changes nothing mathematically; it keeps
- * exp in range). Wabs_c = sum_j w_j * |v_jc| is the magnitude that scales
- * the acceptance bound. Row-major Q (Sq x D, ldq), K (Sk x D, ldk),
- * V (Sk x Dv, ldv), O and Wabs (Sq x Dv, ldo); Sk >= 1; Wabs may be NULL.
- * Returns 0, or -1 if scratch memory cannot be allocated. */
+ * exp in range). Two magnitudes scale the acceptance bound:
+ * Wabs_c = sum_j w_j * |v_jc| and G = max_j sum_d |q_d| * |k_jd| (the size
+ * of the score sums, which fp32 accumulation perturbs). Row-major Q (Sq x D,
+ * ldq), K (Sk x D, ldk), V (Sk x Dv, ldv), O and Wabs (Sq x Dv, ldo), G (Sq);
+ * Sk >= 1; Wabs and G may be NULL. Returns 0, or -1 if scratch memory cannot
+ * be allocated. */
 int oracle_attention_f64(int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
                          const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk,
                          const uint16_t *V, int64_t ldv, double scale, int fmt,
-                         double *O, double *Wabs, int64_t ldo)
+                         double *O, double *Wabs, int64_t ldo, double *G)
 {
     int failed = 0;
     int64_t i;
@@ -186,7 +188,7 @@ int oracle_attention_f64(int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
         double *s = (double *)malloc((size_t)(Sk > 0 ? Sk : 1) * sizeof(double));
         double *q = (double *)malloc((size_t)(D > 0 ? D : 1) * sizeof(double));
         int64_t j, d, c;
-        double mx = -INFINITY, sum = 0.0;
+        double mx = -INFINITY, sum = 0.0, gmax = 0.0;
         if (!s || !q) {
             free(s);
             free(q);
@@ -196,13 +198,20 @@ int oracle_attention_f64(int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
         for (d = 0; d < D; ++d)
             q[d] = oracle_decode16(Q[i * ldq + d], fmt);
         for (j = 0; j < Sk; ++j) {
-            double acc = 0.0;
-            for (d = 0; d < D; ++d)
-                acc += q[d] * oracle_decode16(K[j * ldk + d], fmt);
+            double acc = 0.0, mag = 0.0;
+            for (d = 0; d < D; ++d) {
+                const double k = oracle_decode16(K[j * ldk + d], fmt);
+                acc += q[d] * k;
+                mag += fabs(q[d]) * fabs(k);
+            }
             s[j] = scale * acc;
             if (s[j] > mx)
                 mx = s[j];
+            if (mag > gmax)
+                gmax = mag;
         }
+        if (G)
+            G[i] = gmax;
         for (j = 0; j < Sk; ++j) {
             s[j] = exp(s[j] - mx);
             sum += s[j];

@@ -18,7 +18,7 @@ def _lib_attention(Q, K, V, fmt, scale):
     q, k, v = (_decoded_by_library(x, fmt) for x in (Q, K, V))
     s = scale * (q @ np.swapaxes(k, -1, -2))
     w = scipy.special.softmax(s, axis=-1)
-    return w @ v, w @ np.abs(v)
+    return w @ v, w @ np.abs(v), (np.abs(q) @ np.abs(np.swapaxes(k, -1, -2))).max(axis=-1)
 
 
 def _m(seed, rows, cols, fmt, kind="grid", pad=0):
@@ -35,10 +35,11 @@ def pin_attention_matches_library_softmax(lib, cases=24):
         K = _m(600 + c, Sk, D, fmt, pad=pads[1])
         V = _m(700 + c, Sk, Dv, fmt, pad=pads[2])
         scale = float(rng.uniform(0.05, 3.0))
-        O, W = oracle.attention_f64(Q, K, V, fmt, scale, with_abs=True, lib=lib)
-        Or, Wr = _lib_attention(Q, K, V, fmt, scale)
+        O, W, G = oracle.attention_f64(Q, K, V, fmt, scale, with_abs=True, lib=lib)
+        Or, Wr, Gr = _lib_attention(Q, K, V, fmt, scale)
         assert np.allclose(O, Or, rtol=1e-12, atol=1e-14), (c, np.abs(O - Or).max())
         assert np.allclose(W, Wr, rtol=1e-12, atol=1e-14), c
+        assert np.allclose(G, Gr, rtol=1e-13, atol=0), c
 
 
 def pin_attention_single_key(lib):
@@ -82,7 +83,7 @@ def pin_attention_weights_sum_to_one(lib):
     for fmt in ("bf16", "f16"):
         Q, K = _m(8, 9, 12, fmt), _m(9, 13, 12, fmt)
         V = _m(0, 13, 3, fmt, kind="ones")
-        O, W = oracle.attention_f64(Q, K, V, fmt, 1.7, with_abs=True, lib=lib)
+        O, W, _ = oracle.attention_f64(Q, K, V, fmt, 1.7, with_abs=True, lib=lib)
         assert np.allclose(O, 1.0, rtol=0, atol=1e-14) and np.allclose(W, 1.0, rtol=0, atol=1e-14), fmt
 
 
@@ -146,7 +147,7 @@ def pin_attention_leading_axes(lib):
     O = oracle.attention_f64(Q, K, V, fmt, 0.8, lib=lib)
     for b in range(2):
         for h in range(3):
-            Or, _ = _lib_attention(Q[b, h], K[b, h], V[b, h], fmt, 0.8)
+            Or, _, _ = _lib_attention(Q[b, h], K[b, h], V[b, h], fmt, 0.8)
             assert np.allclose(O[b, h], Or, rtol=1e-12, atol=1e-14), (b, h)
 
 

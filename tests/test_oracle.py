@@ -30,6 +30,14 @@ def test_bound_formula():
     assert np.array_equal(oracle.bound(1024, Abs), 4 * 1024 * 2.0 ** -24 * Abs)
 
 
+def test_attention_bound_formula():
+    W = np.array([[1.0, 0.5]])
+    G = np.array([3.0])
+    b = oracle.attention_bound(W, "bf16", G, -2.0, 64)
+    assert np.allclose(b, (2.0 ** -6 + 4 * 2.0 * 72 * 2.0 ** -24 * 3.0) * W, rtol=1e-15, atol=0)
+    assert np.allclose(oracle.attention_bound(W, "f16", G, 0.0, 64), 2.0 ** -8 * W, rtol=1e-15, atol=0)
+
+
 # Deliberate mistakes planted in copies of the oracle's source. Each must be
 # caught by at least one pin, which shows the pins can see that class of bug.
 MUTANTS = {
@@ -56,6 +64,8 @@ MUTANTS = {
     "attn_abs_keeps_sign": ("Wabs[i * ldo + c] += w * fabs(v);", "Wabs[i * ldo + c] += w * v;"),
     "attn_ignores_ldv": ("V[j * ldv + c]", "V[j * Dv + c]"),
     "attn_ignores_ldq": ("Q[i * ldq + d]", "Q[i * D + d]"),
+    "attn_g_drops_abs_of_k": ("mag += fabs(q[d]) * fabs(k);", "mag += fabs(q[d]) * k;"),
+    "attn_g_of_first_key": ("if (mag > gmax)", "if (j == 0)"),
     "attn_query_shift": ("q[d] = oracle_decode16(Q[i * ldq + d], fmt);", "q[d] = oracle_decode16(Q[((i + 1) % Sq) * ldq + d], fmt);"),
 }
 
