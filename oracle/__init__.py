@@ -14,6 +14,7 @@ import ctypes
 import os
 import subprocess
 import time
+from typing import NamedTuple
 
 import numpy as np
 
@@ -61,7 +62,7 @@ def _bind(lib):
     lib.oracle_gemm16_f64.argtypes = [i64, i64, i64, fp, i64, fp, i64, dp, i64, ctypes.c_int, ctypes.c_int]
     lib.oracle_gemm16_f64.restype = None
     lib.oracle_attention_f64.argtypes = [i64, i64, i64, i64, fp, i64, fp, i64, fp, i64, ctypes.c_double,
-                                         ctypes.c_int, dp, dp, i64, dp]
+                                         ctypes.c_int, dp, dp, i64, dp, dp]
     lib.oracle_attention_f64.restype = ctypes.c_int
     return lib
 
@@ -158,13 +159,22 @@ def timed_gemm_rows(A: np.ndarray, B: np.ndarray, rows: int, lib=None):
     return dt, 2.0 * M * N * K
 
 
+class AttnRef(NamedTuple):
+    """The attention oracle's result and the magnitudes its bound needs."""
+    O: np.ndarray     # (..., Sq, Dv) softmax(scale Q K^T) V
+    Wabs: np.ndarray  # (..., Sq, Dv) sum_j w_j |v_jc|
+    G: np.ndarray     # (..., Sq) max_j sum_d |q_d||k_jd|
+    Vmax: np.ndarray  # (..., Dv) max_j |v_jc|
+    D: int
+    Sk: int
+
+
 def attention_f64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, fmt: str, scale: float, with_abs: bool = False,
                   lib=None):
     """softmax(scale * Q K^T) V in fp64 for 16-bit patterns Q (..., Sq, D),
     K (..., Sk, D), V (..., Sk, Dv) with any leading (batch, head) axes and
-    unit stride along the last axis; returns O (..., Sq, Dv) and, with
-    ``with_abs``, (O, Wabs, G): the weighted magnitudes sum_j w_j |v_jc|
-    (..., Sq, Dv) and the score magnitudes max_j sum_d |q_d||k_jd| (..., Sq)."""
+    unit stride along the last axis; returns O (..., Sq, Dv), or with
+    ``with_abs`` an AttnRef that also carries the magnitudes of the bound."""
     lib = lib or load()
     for name, x in (("Q", Q), ("K", K), ("V", V)):
         if x.dtype != np.uint16 or x.ndim < 2 or (x.size and x.strides[-1] != 2):
@@ -179,33 +189,37 @@ def attention_f64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, fmt: str, scale: 
     if Sk < 1:
         raise ValueError("softmax over an empty key set is undefined")
     O = np.zeros(lead + (Sq, Dv))
-    W = np.zeros(lead + (Sq, Dv)) if with_abs else None
-    G = np.zeros(lead + (Sq,)) if with_abs else None
+    W = np.zeros(lead + (Sq, Dv))
+    G = np.zeros(lead + (Sq,))
+    Vm = np.zeros(lead + (Dv,))
     for idx in np.ndindex(*lead):
         q, k, v = Q[idx], K[idx], V[idx]
-        o = O[idx]
-        w = W[idx] if with_abs else None
-        g = G[idx] if with_abs else None
+        o, w, g, vm = O[idx], W[idx], G[idx], Vm[idx]
         st = lib.oracle_attention_f64(Sq, Sk, D, Dv, _ptr(q), q.strides[0] // 2, _ptr(k), k.strides[0] // 2,
                                       _ptr(v), v.strides[0] // 2, float(scale), FMT[fmt], _ptr(o),
-                                      _ptr(w) if with_abs else None, Dv, _ptr(g) if with_abs else None)
+                                      _ptr(w) if with_abs else None, Dv, _ptr(g) if with_abs else None,
+                                      _ptr(vm) if with_abs else None)
         if st != 0:
             raise MemoryError("oracle_attention_f64: out of memory")
-    return (O, W, G) if with_abs else O
+    return AttnRef(O, W, G, Vm, int(D), int(Sk)) if with_abs else O
 
 
-def attention_bound(Wabs: np.ndarray, fmt: str, G: np.ndarray, scale: float, D: int) -> np.ndarray:
+def attention_bound(ref: AttnRef, fmt: str, scale: float) -> np.ndarray:
     """Acceptance bound of the attention kernels, elementwise:
-    (e_p + 4 delta_i) * sum_j w_j |v_jc|. e_p = 2^-6 (bfloat16) or 2^-8
-    (binary16): the probabilities are rounded to the 16-bit format before the
-    P V product (unit roundoff 2^-8 or 2^-11), which moves each weight by at
-    most about twice that, with fp32 accumulation and rescaling adding far
-    less for key counts below 2^14. delta_i = |scale| (D + 8) 2^-24 G_i bounds
-    the error of every score of query row i (fp32 sums of D exact products,
-    then the fp32 scaling into the exponent and the shift by the row
-    maximum); perturbing every score by at most delta moves each softmax
-    weight by a factor within exp(+-2 delta), so O by at most
-    2 delta sum_j w_j |v_jc|, taken twice."""
+    (e_p + 4 delta_i) sum_j w_j |v_jc| + Sk 2^-125 max_j |v_jc|.
+    e_p = 2^-6 (bfloat16) or 2^-8 (binary16): the probabilities are rounded
+    to the 16-bit format before the P V product (unit roundoff 2^-8 or
+    2^-11), which moves each weight by at most about twice that, with fp32
+    accumulation and rescaling adding far less for key counts below 2^14.
+    delta_i = |scale| (D + 8) 2^-24 G_i bounds the error of every score of
+    query row i (fp32 sums of D exact products, then the fp32 scaling into
+    the exponent and the shift by the row maximum); perturbing every score by
+    at most delta moves each softmax weight by a factor within
+    exp(+-2 delta), so O by at most 2 delta sum_j w_j |v_jc|, taken twice.
+    The last term covers underflow: the kernels' probabilities lie in [0, 1]
+    with a row sum of at least 1 (the row maximum contributes 2^0), and a
+    probability or rescaling factor below fp32's normal range (2^-126) drops
+    at most 2^-126 |v_jc| per key."""
     e_p = 2.0 ** -6 if fmt == "bf16" else 2.0 ** -8
-    delta = abs(scale) * (D + 8) * 2.0 ** -24 * G
-    return (e_p + 4.0 * delta[..., None]) * Wabs
+    delta = abs(scale) * (ref.D + 8) * 2.0 ** -24 * ref.G
+    return (e_p + 4.0 * delta[..., None]) * ref.Wabs + ref.Sk * 2.0 ** -125 * ref.Vmax[..., None, :]

@@ -170,19 +170,31 @@ void oracle_gemm16_f64(int64_t M, int64_t N, int64_t K,
  *   O_c   = sum_j w_j * v_jc                                    (c < Dv)
  * per query row q (i < Sq), all in fp64 from the decoded 16-bit inputs
  * (subtracting the row maximum changes nothing mathematically; it keeps
- * exp in range). Two magnitudes scale the acceptance bound:
- * Wabs_c = sum_j w_j * |v_jc| and G = max_j sum_d |q_d| * |k_jd| (the size
- * of the score sums, which fp32 accumulation perturbs). Row-major Q (Sq x D,
- * ldq), K (Sk x D, ldk), V (Sk x Dv, ldv), O and Wabs (Sq x Dv, ldo), G (Sq);
- * Sk >= 1; Wabs and G may be NULL. Returns 0, or -1 if scratch memory cannot
- * be allocated. */
+ * exp in range). Three magnitudes scale the acceptance bound:
+ * Wabs_c = sum_j w_j * |v_jc|, G = max_j sum_d |q_d| * |k_jd| (the size of
+ * the score sums, which fp32 accumulation perturbs) and, once per call,
+ * Vmax_c = max_j |v_jc| (the size of what an underflowing weight can drop).
+ * Row-major Q (Sq x D, ldq), K (Sk x D, ldk), V (Sk x Dv, ldv), O and Wabs
+ * (Sq x Dv, ldo), G (Sq), Vmax (Dv); Sk >= 1; Wabs, G and Vmax may be NULL.
+ * Returns 0, or -1 if scratch memory cannot be allocated. */
 int oracle_attention_f64(int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
                          const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk,
                          const uint16_t *V, int64_t ldv, double scale, int fmt,
-                         double *O, double *Wabs, int64_t ldo, double *G)
+                         double *O, double *Wabs, int64_t ldo, double *G, double *Vmax)
 {
     int failed = 0;
     int64_t i;
+    if (Vmax) {
+        int64_t j, c;
+        for (c = 0; c < Dv; ++c) {
+            Vmax[c] = 0.0;
+            for (j = 0; j < Sk; ++j) {
+                const double v = fabs(oracle_decode16(V[j * ldv + c], fmt));
+                if (v > Vmax[c])
+                    Vmax[c] = v;
+            }
+        }
+    }
 #pragma omp parallel for schedule(static) reduction(| : failed)
     for (i = 0; i < Sq; ++i) {
         double *s = (double *)malloc((size_t)(Sk > 0 ? Sk : 1) * sizeof(double));

@@ -35,11 +35,12 @@ def pin_attention_matches_library_softmax(lib, cases=24):
         K = _m(600 + c, Sk, D, fmt, pad=pads[1])
         V = _m(700 + c, Sk, Dv, fmt, pad=pads[2])
         scale = float(rng.uniform(0.05, 3.0))
-        O, W, G = oracle.attention_f64(Q, K, V, fmt, scale, with_abs=True, lib=lib)
+        O, W, G, Vm, Dd, Skk = oracle.attention_f64(Q, K, V, fmt, scale, with_abs=True, lib=lib)
         Or, Wr, Gr = _lib_attention(Q, K, V, fmt, scale)
         assert np.allclose(O, Or, rtol=1e-12, atol=1e-14), (c, np.abs(O - Or).max())
         assert np.allclose(W, Wr, rtol=1e-12, atol=1e-14), c
         assert np.allclose(G, Gr, rtol=1e-13, atol=0), c
+        assert np.array_equal(Vm, np.abs(_decoded_by_library(V, fmt)).max(axis=0)) and (Dd, Skk) == (D, Sk), c
 
 
 def pin_attention_single_key(lib):
@@ -83,7 +84,7 @@ def pin_attention_weights_sum_to_one(lib):
     for fmt in ("bf16", "f16"):
         Q, K = _m(8, 9, 12, fmt), _m(9, 13, 12, fmt)
         V = _m(0, 13, 3, fmt, kind="ones")
-        O, W, _ = oracle.attention_f64(Q, K, V, fmt, 1.7, with_abs=True, lib=lib)
+        O, W = oracle.attention_f64(Q, K, V, fmt, 1.7, with_abs=True, lib=lib)[:2]
         assert np.allclose(O, 1.0, rtol=0, atol=1e-14) and np.allclose(W, 1.0, rtol=0, atol=1e-14), fmt
 
 

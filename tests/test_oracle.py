@@ -33,9 +33,12 @@ def test_bound_formula():
 def test_attention_bound_formula():
     W = np.array([[1.0, 0.5]])
     G = np.array([3.0])
-    b = oracle.attention_bound(W, "bf16", G, -2.0, 64)
-    assert np.allclose(b, (2.0 ** -6 + 4 * 2.0 * 72 * 2.0 ** -24 * 3.0) * W, rtol=1e-15, atol=0)
-    assert np.allclose(oracle.attention_bound(W, "f16", G, 0.0, 64), 2.0 ** -8 * W, rtol=1e-15, atol=0)
+    Vm = np.array([2.0, 4.0])
+    ref = oracle.AttnRef(np.zeros_like(W), W, G, Vm, 64, 10)
+    floor = 10 * 2.0 ** -125 * Vm
+    b = oracle.attention_bound(ref, "bf16", -2.0)
+    assert np.allclose(b, (2.0 ** -6 + 4 * 2.0 * 72 * 2.0 ** -24 * 3.0) * W + floor, rtol=1e-15, atol=0)
+    assert np.allclose(oracle.attention_bound(ref, "f16", 0.0), 2.0 ** -8 * W + floor, rtol=1e-15, atol=0)
 
 
 # Deliberate mistakes planted in copies of the oracle's source. Each must be
@@ -66,6 +69,7 @@ MUTANTS = {
     "attn_ignores_ldq": ("Q[i * ldq + d]", "Q[i * D + d]"),
     "attn_g_drops_abs_of_k": ("mag += fabs(q[d]) * fabs(k);", "mag += fabs(q[d]) * k;"),
     "attn_g_of_first_key": ("if (mag > gmax)", "if (j == 0)"),
+    "attn_vmax_keeps_sign": ("const double v = fabs(oracle_decode16(V[j * ldv + c], fmt));", "const double v = oracle_decode16(V[j * ldv + c], fmt);"),
     "attn_query_shift": ("q[d] = oracle_decode16(Q[i * ldq + d], fmt);", "q[d] = oracle_decode16(Q[((i + 1) % Sq) * ldq + d], fmt);"),
 }
 
