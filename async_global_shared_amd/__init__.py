@@ -67,13 +67,17 @@ def lib():
         L.mgemm_gemm16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, vp]
         L.mgemm_plan_gemm16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci,
                                         ctypes.POINTER(Plan)]
+        L.mgemm_attention.argtypes = [i64, i64, i64, i64, i64, vp, i64, i64, i64, vp, i64, i64, i64, vp, i64, i64,
+                                      i64, vp, i64, i64, i64, ctypes.c_float, ci, ci, ci, vp]
+        L.mgemm_plan_attention.argtypes = [i64, i64, i64, i64, i64, vp, i64, i64, i64, vp, i64, i64, i64, vp, i64,
+                                           i64, i64, vp, i64, i64, i64, ci, ci, ci, ctypes.POINTER(Plan)]
         L.mgemm_blocks_per_cu.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci,
                                           ctypes.POINTER(ctypes.c_int)]
         L.mgemm_status_string.argtypes = [ci]
         L.mgemm_status_string.restype = ctypes.c_char_p
         for f in (L.mgemm_sgemm, L.mgemm_sgemm_ex, L.mgemm_tile_copy, L.mgemm_plan_sgemm,
                   L.mgemm_ring_trace, L.mgemm_version, L.mgemm_blocks_per_cu, L.mgemm_gemm16,
-                  L.mgemm_plan_gemm16):
+                  L.mgemm_plan_gemm16, L.mgemm_attention, L.mgemm_plan_attention):
             f.restype = ci
         _lib = L
     return _lib
@@ -96,6 +100,21 @@ def mgemm_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile
 def mgemm_plan_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile):
     p = Plan()
     st = lib().mgemm_plan_gemm16(M, N, K, A, lda, B, ldb, C, ldc, dtype, stages, fill_mode, tile, ctypes.byref(p))
+    return st, p
+
+
+def mgemm_attention(batch, heads, seq_q, seq_k, head_dim, Q, q_sb, q_sh, q_ld, K, k_sb, k_sh, k_ld, V, v_sb, v_sh,
+                    v_ld, O, o_sb, o_sh, o_ld, scale, dtype, stages, fill_mode, stream) -> int:
+    return lib().mgemm_attention(batch, heads, seq_q, seq_k, head_dim, Q, q_sb, q_sh, q_ld, K, k_sb, k_sh, k_ld, V,
+                                 v_sb, v_sh, v_ld, O, o_sb, o_sh, o_ld, scale, dtype, stages, fill_mode, stream)
+
+
+def mgemm_plan_attention(batch, heads, seq_q, seq_k, head_dim, Q, q_sb, q_sh, q_ld, K, k_sb, k_sh, k_ld, V, v_sb,
+                         v_sh, v_ld, O, o_sb, o_sh, o_ld, dtype, stages, fill_mode):
+    p = Plan()
+    st = lib().mgemm_plan_attention(batch, heads, seq_q, seq_k, head_dim, Q, q_sb, q_sh, q_ld, K, k_sb, k_sh, k_ld,
+                                    V, v_sb, v_sh, v_ld, O, o_sb, o_sh, o_ld, dtype, stages, fill_mode,
+                                    ctypes.byref(p))
     return st, p
 
 
@@ -217,6 +236,57 @@ def plan16(M, N, K, *, dtype="bf16", stages=2, fill="piped", tile="auto", lda=No
                               _FILL[fill], _TILE[tile])
     if st != OK:
         raise MgemmError(st, "mgemm_plan_gemm16")
+    return p.as_dict()
+
+
+def _attn_view(t, name, fp32=False):
+    import torch
+    want = (torch.float32,) if fp32 else (torch.bfloat16, torch.float16)
+    if not isinstance(t, torch.Tensor) or t.dim() != 4 or t.dtype not in want:
+        raise TypeError(f"{name} must be a 4-D (batch, heads, seq, dim) torch tensor of "
+                        f"{'float32' if fp32 else 'bfloat16 or float16'}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be on a GPU")
+    if t.numel() and t.stride(3) != 1:
+        raise TypeError(f"{name} must have unit stride along its last axis")
+    sb, sh, ld, _ = t.stride()
+    return t.data_ptr(), sb, sh, ld
+
+
+def attention(Q, K, V, O=None, *, scale=None, stages: int = 2, fill: str = "piped", stream=None):
+    """O (fp32) = softmax(scale Q K^T) V per (batch, head) through
+    mgemm_attention; Q (B, H, Sq, D), K and V (B, H, Sk, D) of one 16-bit
+    format; scale defaults to 1/sqrt(D)."""
+    import torch
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K and V must have the same 16-bit format")
+    B, H, Sq, D = Q.shape
+    Sk = K.shape[2]
+    if K.shape != (B, H, Sk, D) or V.shape != (B, H, Sk, D):
+        raise ValueError("K and V must be (batch, heads, seq_k, head_dim) matching Q")
+    if O is None:
+        O = torch.empty((B, H, Sq, D), dtype=torch.float32, device=Q.device)
+    scale = D ** -0.5 if scale is None else float(scale)
+    q, k, v = _attn_view(Q, "Q"), _attn_view(K, "K"), _attn_view(V, "V")
+    o = _attn_view(O, "O", fp32=True)
+    dtype = DTYPE_BF16 if Q.dtype == torch.bfloat16 else DTYPE_F16
+    st = mgemm_attention(B, H, Sq, Sk, D, *q, *k, *v, *o, scale, dtype, stages, _FILL[fill], _stream(stream))
+    if st != OK:
+        raise MgemmError(st, "mgemm_attention")
+    return O
+
+
+def plan_attention(batch, heads, seq_q, seq_k, head_dim, *, dtype="bf16", stages=2, fill="piped", align=16):
+    """Launch plan of attention on contiguous (batch, heads, seq, dim)
+    tensors at fake addresses aligned to `align` bytes (no device access)."""
+    D = head_dim
+    qa, ka, va, oa = (1 << 32) + align % 16, 1 << 36, 1 << 37, 1 << 40
+    st, p = mgemm_plan_attention(batch, heads, seq_q, seq_k, D, qa, heads * seq_q * D, seq_q * D, D,
+                                 ka, heads * seq_k * D, seq_k * D, D, va, heads * seq_k * D, seq_k * D, D,
+                                 oa, heads * seq_q * D, seq_q * D, D, DTYPE_BF16 if dtype == "bf16" else DTYPE_F16,
+                                 stages, _FILL[fill])
+    if st != OK:
+        raise MgemmError(st, "mgemm_plan_attention")
     return p.as_dict()
 
 

@@ -588,11 +588,13 @@ struct CfgH256x256 { // 8 waves (2 per SIMD), each 128 x 64 as in the 256 x 128 
 // b % 8), each with its own L2. Give each XCD a contiguous range of logical
 // tiles, then walk the logical order a few tile-rows down before moving right, so
 // the blocks resident on one XCD share A and B panels in its L2.
-__device__ inline void block_tile(int bid, int gm, int gn, int &tm, int &tn) {
-    const int nb = gm * gn;
+__device__ inline int xcd_linear(int bid, int nb) {
     const int x = bid & 7, i = bid >> 3;
     const int q = nb >> 3, r = nb & 7;
-    const int lin = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+    return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+__device__ inline void block_tile(int bid, int gm, int gn, int &tm, int &tn) {
+    const int lin = xcd_linear(bid, gm * gn);
     constexpr int G = MGEMM_GROUP_ROWS;
     const int per_group = G * gn;
     const int grp = lin / per_group;

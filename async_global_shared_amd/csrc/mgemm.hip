@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "attention.hpp"
 #include "device.hpp"
 #include "mgemm.h"
 
@@ -187,6 +188,18 @@ MG_COPY_INST(3)
 MG_COPY_INST(4)
 MG_COPY_INST(5)
 MG_COPY_INST(6)
+#define MG_ATTN_INST(D, BF, S, W)                                                                        \
+    template __global__ void mgemm::attention_kernel<D, BF, S, true, W>(mgemm::AttnArgs);                \
+    template __global__ void mgemm::attention_kernel<D, BF, S, false, W>(mgemm::AttnArgs);
+#define MG_ATTN_CFG(D, BF)                                                                               \
+    MG_ATTN_INST(D, BF, 1, 16) MG_ATTN_INST(D, BF, 2, 16) MG_ATTN_INST(D, BF, 3, 16)                     \
+    MG_ATTN_INST(D, BF, 1, 4) MG_ATTN_INST(D, BF, 2, 4) MG_ATTN_INST(D, BF, 3, 4)                        \
+    template __global__ void mgemm::attention_kernel<D, BF, 4, true, 16>(mgemm::AttnArgs);               \
+    template __global__ void mgemm::attention_kernel<D, BF, 4, true, 4>(mgemm::AttnArgs);
+MG_ATTN_CFG(64, true)
+MG_ATTN_CFG(64, false)
+MG_ATTN_CFG(128, true)
+MG_ATTN_CFG(128, false)
 
 namespace {
 
@@ -370,6 +383,113 @@ struct Recorder {
     template <int SET>
     void load(int s) { put(6, s, SET); }
 };
+
+
+// ---- attention ----------------------------------------------------------------------
+
+// [lo, hi) byte range of a (batch, heads, rows, cols) view of `esize`-byte elements
+Range span4(const void *p, int64_t batch, int64_t heads, int64_t rows, int64_t cols, int64_t sb, int64_t sh,
+            int64_t ld, int esize) {
+    Range r;
+    if (batch > 0 && heads > 0 && rows > 0 && cols > 0) {
+        r.lo = reinterpret_cast<uintptr_t>(p);
+        r.hi = r.lo + (uintptr_t)(((batch - 1) * sb + (heads - 1) * sh + (rows - 1) * ld + cols) * esize);
+    }
+    return r;
+}
+
+struct AttnView {
+    const void *p;
+    int64_t sb, sh, ld;
+};
+
+int check_view16(const AttnView &v, int64_t rows, int64_t D) {
+    if (v.p == nullptr || v.sb < 0 || v.sh < 0 || v.ld < D)
+        return MGEMM_ERR_ARG;
+    // pairs of 16-bit elements are moved as 32-bit words
+    if ((reinterpret_cast<uintptr_t>(v.p) & 3) || v.sb % 2 || v.sh % 2 || v.ld % 2)
+        return MGEMM_ERR_ARG;
+    if (v.ld / 2 >= kMaxLd || rows >= kMaxExtent)
+        return MGEMM_ERR_UNSUPPORTED;
+    return MGEMM_OK;
+}
+bool view16_b128(const AttnView &v) { return aligned16(v.p) && v.sb % 8 == 0 && v.sh % 8 == 0 && v.ld % 8 == 0; }
+
+int plan_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t D, const AttnView &q,
+                   const AttnView &k, const AttnView &v, const AttnView &o, int dtype, int stages, int fill,
+                   mgemm_plan_t *pl) {
+    if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || (D != 64 && D != 128) ||
+        (dtype != MGEMM_DTYPE_BF16 && dtype != MGEMM_DTYPE_F16) || stages < 1 ||
+        stages > (fill == MGEMM_FILL_PIPED ? kMaxStages16 : kMaxSyncStages) ||
+        (fill != MGEMM_FILL_SYNC && fill != MGEMM_FILL_PIPED))
+        return MGEMM_ERR_ARG;
+    const bool work = batch > 0 && heads > 0 && seq_q > 0;
+    mgemm_plan_t p;
+    std::memset(&p, 0, sizeof p);
+    p.compute = MGEMM_COMPUTE_MFMA;
+    p.bm = kAttnBQ;
+    p.bn = (int)D;
+    p.bk = kAttnBK;
+    p.threads = kAttnThreads;
+    p.stages = stages;
+    p.fill_mode = fill;
+    if (work) {
+        if (seq_k == 0) // softmax over no keys is undefined
+            return MGEMM_ERR_ARG;
+        int st;
+        if ((st = check_view16(q, seq_q, D)) != MGEMM_OK || (st = check_view16(k, seq_k, D)) != MGEMM_OK ||
+            (st = check_view16(v, seq_k, D)) != MGEMM_OK)
+            return st;
+        if (o.p == nullptr || o.sb < 0 || o.sh < 0 || o.ld < D || (reinterpret_cast<uintptr_t>(o.p) & 3))
+            return MGEMM_ERR_ARG;
+        if (o.ld >= kMaxLd)
+            return MGEMM_ERR_UNSUPPORTED;
+        const int64_t nqb = (seq_q + kAttnBQ - 1) / kAttnBQ;
+        if (seq_q >= kMaxExtent || seq_k >= kMaxExtent || batch * heads >= kMaxExtent ||
+            batch * heads * nqb >= kMaxExtent)
+            return MGEMM_ERR_UNSUPPORTED;
+        const Range ro = span4(o.p, batch, heads, seq_q, D, o.sb, o.sh, o.ld, 4);
+        if (overlap(ro, span4(q.p, batch, heads, seq_q, D, q.sb, q.sh, q.ld, 2)) ||
+            overlap(ro, span4(k.p, batch, heads, seq_k, D, k.sb, k.sh, k.ld, 2)) ||
+            overlap(ro, span4(v.p, batch, heads, seq_k, D, v.sb, v.sh, v.ld, 2)))
+            return MGEMM_ERR_ALIAS;
+        p.blocks = (int)(batch * heads * nqb);
+        p.slices = (int)((seq_k + kAttnBK - 1) / kAttnBK);
+    }
+    const int W = (view16_b128(q) && view16_b128(k) && view16_b128(v)) ? 16 : 4;
+    p.load_bytes = W;
+    const int slice_bytes = 2 * kAttnBK * (int)D * 2; // a K and a V tile
+    p.lds_bytes = stages * slice_bytes;
+    p.loads_per_slice = slice_bytes / (64 * W) / kAttnWaves;
+    p.max_vmcnt = fill == MGEMM_FILL_PIPED ? std::min(63, std::max(0, stages - 2) * p.loads_per_slice) : 0;
+    if (p.lds_bytes > kLdsBytes)
+        return MGEMM_ERR_UNSUPPORTED;
+    if (pl)
+        *pl = p;
+    return MGEMM_OK;
+}
+
+template <int D, bool BF, int W>
+const void *attention_kernel_w(int S, int fill) {
+    const bool piped = fill == MGEMM_FILL_PIPED;
+    switch (S) {
+    case 1: return piped ? (const void *)&attention_kernel<D, BF, 1, true, W> : (const void *)&attention_kernel<D, BF, 1, false, W>;
+    case 2: return piped ? (const void *)&attention_kernel<D, BF, 2, true, W> : (const void *)&attention_kernel<D, BF, 2, false, W>;
+    case 3: return piped ? (const void *)&attention_kernel<D, BF, 3, true, W> : (const void *)&attention_kernel<D, BF, 3, false, W>;
+    default: return (const void *)&attention_kernel<D, BF, 4, true, W>; // piped only
+    }
+}
+template <int D, bool BF>
+const void *attention_kernel_d(const mgemm_plan_t &p) {
+    return p.load_bytes == 16 ? attention_kernel_w<D, BF, 16>(p.stages, p.fill_mode)
+                              : attention_kernel_w<D, BF, 4>(p.stages, p.fill_mode);
+}
+const void *select_attention(const mgemm_plan_t &p, int dtype) {
+    const bool bf = dtype == MGEMM_DTYPE_BF16;
+    if (p.bn == 64)
+        return bf ? attention_kernel_d<64, true>(p) : attention_kernel_d<64, false>(p);
+    return bf ? attention_kernel_d<128, true>(p) : attention_kernel_d<128, false>(p);
+}
 
 } // namespace
 
@@ -569,6 +689,58 @@ int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *event
         }
     }
     return r.n;
+}
+
+int mgemm_plan_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                         const void *Q, int64_t q_sb, int64_t q_sh, int64_t q_ld, const void *K, int64_t k_sb,
+                         int64_t k_sh, int64_t k_ld, const void *V, int64_t v_sb, int64_t v_sh, int64_t v_ld,
+                         const float *O, int64_t o_sb, int64_t o_sh, int64_t o_ld, int dtype, int stages,
+                         int fill_mode, mgemm_plan_t *plan) {
+    return plan_attention(batch, heads, seq_q, seq_k, head_dim, {Q, q_sb, q_sh, q_ld}, {K, k_sb, k_sh, k_ld},
+                          {V, v_sb, v_sh, v_ld}, {O, o_sb, o_sh, o_ld}, dtype, stages, fill_mode, plan);
+}
+
+int mgemm_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim, const void *Q,
+                    int64_t q_sb, int64_t q_sh, int64_t q_ld, const void *K, int64_t k_sb, int64_t k_sh,
+                    int64_t k_ld, const void *V, int64_t v_sb, int64_t v_sh, int64_t v_ld, float *O, int64_t o_sb,
+                    int64_t o_sh, int64_t o_ld, float scale, int dtype, int stages, int fill_mode, void *stream) {
+    mgemm_plan_t p;
+    int st = plan_attention(batch, heads, seq_q, seq_k, head_dim, {Q, q_sb, q_sh, q_ld}, {K, k_sb, k_sh, k_ld},
+                            {V, v_sb, v_sh, v_ld}, {O, o_sb, o_sh, o_ld}, dtype, stages, fill_mode, &p);
+    if (st != MGEMM_OK)
+        return st;
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return MGEMM_ERR_ARG;
+    if (batch == 0 || heads == 0 || seq_q == 0)
+        return MGEMM_OK;
+    int dev;
+    if ((st = current_device(&dev)) != MGEMM_OK)
+        return st;
+    AttnArgs a;
+    a.Q = static_cast<const float *>(Q);
+    a.K = static_cast<const float *>(K);
+    a.V = static_cast<const float *>(V);
+    a.O = O;
+    a.q_sb = q_sb / 2;
+    a.q_sh = q_sh / 2;
+    a.k_sb = k_sb / 2;
+    a.k_sh = k_sh / 2;
+    a.v_sb = v_sb / 2;
+    a.v_sh = v_sh / 2;
+    a.o_sb = o_sb;
+    a.o_sh = o_sh;
+    a.q_ld = (int)(q_ld / 2);
+    a.k_ld = (int)(k_ld / 2);
+    a.v_ld = (int)(v_ld / 2);
+    a.o_ld = (int)o_ld;
+    a.heads = (int)heads;
+    a.seq_q = (int)seq_q;
+    a.seq_k = (int)seq_k;
+    a.nqb = (int)((seq_q + kAttnBQ - 1) / kAttnBQ);
+    a.nblocks = p.blocks;
+    a.c = (float)((double)scale * 1.4426950408889634); // log2(e)
+    a.vec_store = aligned16(O) && o_sb % 4 == 0 && o_sh % 4 == 0 && o_ld % 4 == 0;
+    return launch(select_attention(p, dtype), p.blocks, &a, reinterpret_cast<hipStream_t>(stream), p.threads);
 }
 
 } // extern "C"

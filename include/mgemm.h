@@ -111,9 +111,9 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K,
 /*
  * C[0:M, 0:N] = A[0:M, 0:K] * B[0:K, 0:N] for 16-bit A and B (dtype
  * MGEMM_DTYPE_BF16 or MGEMM_DTYPE_F16, the same format for both) and fp32 C:
- * the tensor-core GEMM "fed by the same pipeline" that the day-74 lesson
- * points to for a later lesson, here v_mfma_f32_32x32x16_{bf16,f16} on the
- * same asynchronous LDS ring (64-element K slices). Products and sums are
+ * the tensor-core GEMM that the day-74 lesson names as the next user of its
+ * pipeline, here v_mfma_f32_32x32x16_{bf16,f16} on the same asynchronous LDS
+ * ring (64-element K slices). Products and sums are
  * fp32 inside the MFMA. lda and ldb count 16-bit elements, ldc fp32
  * elements. Requirements (else MGEMM_ERR_ARG): K, N, lda and ldb even; A and
  * B 4-byte aligned. stages 1 .. 4 (piped) or 1 .. 3 (sync); fill_mode MGEMM_FILL_SYNC or
@@ -135,6 +135,43 @@ int mgemm_plan_gemm16(int64_t M, int64_t N, int64_t K,
                       const float *C, int64_t ldc,
                       int dtype, int stages, int fill_mode, int tile,
                       struct mgemm_plan *plan);
+
+/*
+ * Scaled dot-product attention forward ("A study on CUDA async memcpy", the
+ * FlashAttention tile pipeline section: the Q tile stays put, K/V tiles
+ * stream through the asynchronous LDS ring while the current one is scored,
+ * and each step rescales and accumulates the running output):
+ *   O[b,h,i,:] = sum_j w_ij V[b,h,j,:],
+ *   w_ij = exp(scale * Q[b,h,i,:].K[b,h,j,:]) / sum_t exp(scale * Q[b,h,i,:].K[b,h,t,:])
+ * for b < batch, h < heads, i < seq_q, j < seq_k. Q, K and V hold 16-bit
+ * elements of format dtype (MGEMM_DTYPE_BF16 / _F16), O is fp32; element
+ * (b, h, i, d) of X is at X + b*x_sb + h*x_sh + i*x_ld + d (element
+ * strides), d < head_dim, head_dim 64 or 128 (the value dimension equals
+ * it). Scores and the P.V product accumulate in fp32 on
+ * v_mfma_f32_32x32x16_{bf16,f16}; the probabilities enter that product
+ * rounded to the input format. Caller-owned device buffers, asynchronous on
+ * `stream`, no allocation. Requirements (else MGEMM_ERR_ARG): Q, K, V 4-byte
+ * aligned with even strides, every ld >= head_dim, O 4-byte aligned,
+ * seq_k >= 1 whenever there is a query (softmax over no keys is undefined),
+ * finite scale, stages 1 .. 4 (piped) or 1 .. 3 (sync), fill_mode
+ * MGEMM_FILL_SYNC or MGEMM_FILL_PIPED (bit-identical results). O must not
+ * overlap Q, K or V (MGEMM_ERR_ALIAS). batch, heads or seq_q == 0 is a no-op.
+ */
+int mgemm_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                    const void *Q, int64_t q_sb, int64_t q_sh, int64_t q_ld,
+                    const void *K, int64_t k_sb, int64_t k_sh, int64_t k_ld,
+                    const void *V, int64_t v_sb, int64_t v_sh, int64_t v_ld,
+                    float *O, int64_t o_sb, int64_t o_sh, int64_t o_ld,
+                    float scale, int dtype, int stages, int fill_mode, void *stream);
+
+/* The launch mgemm_attention would make (no device access): bm = queries
+ * per block, bn = head_dim, bk = keys per ring slice; as mgemm_plan_sgemm. */
+int mgemm_plan_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                         const void *Q, int64_t q_sb, int64_t q_sh, int64_t q_ld,
+                         const void *K, int64_t k_sb, int64_t k_sh, int64_t k_ld,
+                         const void *V, int64_t v_sb, int64_t v_sh, int64_t v_ld,
+                         const float *O, int64_t o_sb, int64_t o_sh, int64_t o_ld,
+                         int dtype, int stages, int fill_mode, struct mgemm_plan *plan);
 
 /*
  * dst[0:rows, 0:cols] = src[0:rows, 0:cols], streamed global -> LDS -> global

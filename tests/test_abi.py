@@ -602,3 +602,95 @@ def test_isa_gemm16_reads_are_waited_for(isa, cfg):
                 for piped in (True, False):
                     bad = _early_uses_of_lds_results(isa[_name16(cfg, bf16, S, piped, W)])
                     assert not bad, (cfg, bf16, S, W, piped, bad[:3])
+
+
+# ---- attention: validation, plans, ISA -----------------------------------------
+
+def att(B=2, H=3, Sq=100, Sk=90, D=64, Q=A0, K=B0, V=B0 + (1 << 24), O=C0, q=None, k=None, v=None, o=None,
+        dtype=1, stages=2, fill=1):
+    """(status, plan) for contiguous (B, H, S, D) views unless strides are given."""
+    q = q or (H * Sq * D, Sq * D, D)
+    k = k or (H * Sk * D, Sk * D, D)
+    v = v or (H * Sk * D, Sk * D, D)
+    o = o or (H * Sq * D, Sq * D, D)
+    return m.mgemm_plan_attention(B, H, Sq, Sk, D, Q, *q, K, *k, V, *v, O, *o, dtype, stages, fill)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=96), m.ERR_ARG), (dict(D=0), m.ERR_ARG), (dict(B=-1), m.ERR_ARG), (dict(Sk=0), m.ERR_ARG),
+    (dict(dtype=0), m.ERR_ARG), (dict(stages=0), m.ERR_ARG), (dict(stages=5), m.ERR_ARG),
+    (dict(stages=4, fill=0), m.ERR_ARG), (dict(fill=2), m.ERR_ARG), (dict(Q=0), m.ERR_ARG), (dict(O=0), m.ERR_ARG),
+    (dict(Q=A0 + 2), m.ERR_ARG), (dict(k=(3 * 90 * 64, 90 * 64, 63)), m.ERR_ARG), (dict(v=(3 * 90 * 64, 90 * 64, 65)), m.ERR_ARG),
+    (dict(o=(3 * 100 * 64, 100 * 64, 63)), m.ERR_ARG), (dict(O=A0), m.ERR_ALIAS), (dict(O=B0 + 64), m.ERR_ALIAS),
+    (dict(q=(0, 0, 1 << 22)), m.ERR_UNSUPPORTED),
+    (dict(Sk=0, Sq=0), m.OK), (dict(B=0, Q=0, K=0, V=0, O=0), m.OK), (dict(Q=A0 + 4), m.OK), (dict(stages=4), m.OK),
+])
+def test_attention_validation(kw, want):
+    st, _ = att(**kw)
+    assert st == want
+    if want != m.OK:
+        a = dict(B=2, H=3, Sq=100, Sk=90, D=64, Q=A0, K=B0, V=B0 + (1 << 24), O=C0, q=None, k=None, v=None, o=None,
+                 dtype=1, stages=2, fill=1)
+        a.update(kw)
+        q = a["q"] or (a["H"] * a["Sq"] * a["D"], a["Sq"] * a["D"], a["D"])
+        k = a["k"] or (a["H"] * a["Sk"] * a["D"], a["Sk"] * a["D"], a["D"])
+        v = a["v"] or (a["H"] * a["Sk"] * a["D"], a["Sk"] * a["D"], a["D"])
+        o = a["o"] or (a["H"] * a["Sq"] * a["D"], a["Sq"] * a["D"], a["D"])
+        # the launching entry point refuses the same arguments before any HIP call
+        assert m.mgemm_attention(a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["Q"], *q, a["K"], *k, a["V"], *v,
+                                 a["O"], *o, 0.125, a["dtype"], a["stages"], a["fill"], None) == want
+
+
+def test_attention_rejects_nonfinite_scale():
+    for s in (float("nan"), float("inf"), float("-inf")):
+        assert m.mgemm_attention(1, 1, 8, 8, 64, A0, 512, 512, 64, B0, 512, 512, 64, B0 + 4096, 512, 512, 64,
+                                 C0, 512, 512, 64, s, 1, 2, 1, None) == m.ERR_ARG
+
+
+def test_attention_plans():
+    p = m.plan_attention(16, 16, 4096, 4096, 128)
+    assert (p["bm"], p["bn"], p["bk"], p["threads"], p["blocks"]) == (128, 128, 64, 256, 16 * 16 * 32)
+    assert p["slices"] == 64 and p["load_bytes"] == 16 and p["lds_bytes"] == 2 * 2 * 64 * 128 * 2
+    # one slice: a 64 x 128 K tile and a V tile, 32 KiB = 8 dwordx4 per lane of each of 4 waves
+    assert p["loads_per_slice"] == 8 and p["max_vmcnt"] == 0
+    assert m.plan_attention(16, 16, 4096, 4096, 128, stages=4)["max_vmcnt"] == 16
+    p = m.plan_attention(1, 3, 200, 300, 64, stages=3, fill="sync", align=4)
+    assert p["load_bytes"] == 4 and p["blocks"] == 3 * 2 and p["slices"] == 5 and p["loads_per_slice"] == 16
+    # the (batch, seq, head, dim) layout keeps 16-byte loads when its strides allow
+    st, p = att(B=2, H=4, Sq=64, Sk=64, D=128, q=(64 * 4 * 128, 128, 4 * 128), k=(64 * 4 * 128, 128, 4 * 128),
+                v=(64 * 4 * 128, 128, 4 * 128))
+    assert st == m.OK and p.load_bytes == 16
+
+
+def _attn_name(D, bf16, S, piped, W):
+    return f"_ZN5mgemm16attention_kernelILi{D}ELb{int(bf16)}ELi{S}ELb{int(piped)}ELi{W}EEEvNS_8AttnArgsE"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_isa_attention(isa, D):
+    """The attention kernels score and accumulate on the 16-bit MFMA (two
+    products per slice), exponentiate with v_exp_f32, pair lanes with
+    v_permlane32_swap, read V through the transposing LDS read, fill the ring
+    asynchronously (piped) or through VGPRs (sync), never drain the prefetch
+    before the MFMAs and never touch an LDS read's result before its wait."""
+    for bf16 in (True, False):
+        mfma = "v_mfma_f32_32x32x16_" + ("bf16" if bf16 else "f16")
+        per_slice = (D // 16) * 2 + (64 // 16) * (D // 32)
+        for S in (1, 2, 3, 4):
+            for W in (16, 4):
+                for piped in ((True, False) if S < 4 else (True,)):
+                    lines = isa[_attn_name(D, bf16, S, piped, W)]
+                    body = "\n".join(lines)
+                    assert body.count(mfma) >= per_slice, (D, bf16, S, W, piped)
+                    assert body.count("v_exp_f32") >= 33 and "v_permlane32_swap" in body
+                    assert "ds_read_b64_tr_b16" in body and "ds_read_b128" in body
+                    width = "dwordx4" if W == 16 else "dword"
+                    if piped:
+                        assert re.search(rf"buffer_load_{width} .* lds", body) and "ds_write" not in body
+                        if S >= 2:
+                            drained, reached = _drain_before_compute(lines, mfma)
+                            assert reached and not drained, (D, S, W)
+                    else:
+                        assert "ds_write" in body and not re.search(r"buffer_load\S* .* lds", body)
+                    assert not _early_uses_of_lds_results(lines), (D, bf16, S, W, piped)
+                    assert "v_pk_fma_f32" not in body and "v_pk_add_f32" not in body and "v_pk_mul_f32" not in body
