@@ -397,8 +397,12 @@ struct AttnSyncOps : AttnCtx<Tile, W> {
     }
 };
 
+#ifndef MGEMM_ATTN_WAVES_PER_EU
+#define MGEMM_ATTN_WAVES_PER_EU 2 // two waves per SIMD: one wave's softmax overlaps the other's MFMAs
+#endif
 template <int D, bool BF16, int S, bool PIPED, int W>
-__global__ void __launch_bounds__(kAttnThreads) attention_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kAttnThreads)
+    __attribute__((amdgpu_waves_per_eu(MGEMM_ATTN_WAVES_PER_EU))) attention_kernel(AttnArgs a) {
     using Tile = AttnTile<D, BF16>;
     using Ctx = AttnCtx<Tile, W>;
     constexpr bool kFits = S * Ctx::SLOT <= kLdsBytes;
