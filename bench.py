@@ -35,8 +35,8 @@ COPY_VIEWS = ((16384, 16384), (4194304, 64))
 
 
 KERNEL_SOURCES = ("async_global_shared_amd/csrc/device.hpp", "async_global_shared_amd/csrc/ring.h",
-                  "async_global_shared_amd/csrc/mgemm.hip")
-COUNTERS_FILE = "profiles/counters_gemm8192_and_copy1GiB.txt"
+                  "async_global_shared_amd/csrc/attention.hpp", "async_global_shared_amd/csrc/mgemm.hip")
+COUNTERS_FILE = "profiles/counters_gemm8192_copy1GiB_gemm16_attention.txt"
 
 
 def kernel_source_hash() -> str:
@@ -85,15 +85,17 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the tables after the timed region")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     p.add_argument("--profile", action="store_true",
-                   help="only run a few launches of the timed GEMM, the 1 GiB tile copy (3 stages) and a plain "
-                        "1 GiB device copy (the calibration kernel for hardware byte counters), for rocprofv3")
+                   help="only run a few launches of the timed GEMM, the 1 GiB tile copy (3 stages), a plain "
+                        "1 GiB device copy (the calibration kernel for hardware byte counters), the 16-bit GEMM "
+                        "and the attention kernel, for rocprofv3")
     return p.parse_args()
 
 
 def profile_mode(args):
     """Launches for counter collection, `steps` of each, no timing: the timed
-    GEMM, its VALU twin, the 1 GiB tile copy in both array views, and a plain
-    1 GiB device copy (the calibration kernel for hardware byte counters)."""
+    GEMM, its VALU twin, the 1 GiB tile copy in both array views, a plain
+    1 GiB device copy (the calibration kernel for hardware byte counters),
+    the 16-bit GEMM and the attention kernel in their default plans."""
     import torch
 
     import async_global_shared_amd as m
@@ -119,6 +121,24 @@ def profile_mode(args):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"profile: {args.steps} x plain device copy 1 GiB (calibration: 2^30 B read, 2^30 B written)", flush=True)
+    del src, dst
+    A16 = datagen.grid16_torch(datagen.SEED_A, n, n, "bf16", device="cuda")
+    B16 = datagen.grid16_torch(datagen.SEED_B, n, n, "bf16", device="cuda")
+    C = torch.empty((n, n), device="cuda")
+    for _ in range(args.steps):
+        m.gemm16(A16, B16, C)
+    torch.cuda.synchronize()
+    print(f"profile: {args.steps} x gemm16 {n}^3 bf16, default plan {m.plan16(n, n, n)}", flush=True)
+    del A16, B16, C
+    B_, H_, S_ = ATTN_SHAPE
+    Q, K, V = (datagen.grid16_torch(seed, 1, B_ * H_ * S_ * 128, "bf16", device="cuda").view(B_, H_, S_, 128)
+               for seed in (datagen.SEED_A, datagen.SEED_B, datagen.SEED_COPY))
+    O = torch.empty((B_, H_, S_, 128), device="cuda")
+    for _ in range(args.steps):
+        m.attention(Q, K, V, O)
+    torch.cuda.synchronize()
+    print(f"profile: {args.steps} x attention {B_}x{H_}x{S_}x128 bf16, default plan "
+          f"{m.plan_attention(B_, H_, S_, S_, 128)}", flush=True)
 
 
 def timed_launches(fn, warmup=3, runs=10, repeats=1):
@@ -276,6 +296,7 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
     res["gemm"] = gemm
     res["stage_study"] = stage_study(m, torch, Ad8, Bd8, Cd8)
     res["gemm16"] = gemm16_table(m, datagen, torch, sorted({min(4096, big), big}))
+    res["attention"] = attention_table(m, datagen, torch)
     # tile copy: 1 GiB fp32 ~ N(0,1), 64x64 tiles, 2 x bytes moved
     n_el = 1 << 28
     src = datagen.normal01_torch(datagen.SEED_COPY, n_el, device="cuda")
@@ -339,6 +360,50 @@ def gemm16_table(m, datagen, torch, sizes):
             row["best"] = best
             out[f"{fmt}_{n}"] = row
             del A, B, C, C1
+    return out
+
+
+ATTN_SHAPE = (16, 16, 4096)  # batch, heads, sequence length (queries = keys)
+
+
+def attention_table(m, datagen, torch):
+    """Attention forward (softmax(Q K^T / sqrt(D)) V, 16-bit Q, K, V, fp32 O)
+    at batch 16, 16 heads, 4096 queries and keys, head dims 128 and 64:
+    TFLOP/s (4 B H Sq Sk D per call) and share of the 2.5 PFLOP/s dense 16-bit
+    MFMA peak per fill and ring depth, after a bitwise piped == sync gate on
+    the whole output; torch's scaled_dot_product_attention as context."""
+    import torch.nn.functional as F
+    B, H, S = ATTN_SHAPE
+    out = {}
+    for fmt in ("bf16", "f16"):
+        for D in (128, 64):
+            Q, K, V = (datagen.grid16_torch(seed, 1, B * H * S * D, fmt, device="cuda").view(B, H, S, D)
+                       for seed in (datagen.SEED_A, datagen.SEED_B, datagen.SEED_COPY))
+            O = torch.empty((B, H, S, D), device="cuda")
+            O1 = torch.empty_like(O)
+            flop = 4.0 * B * H * S * S * D
+            row = {}
+            for fill in ("sync", "piped"):
+                for St in (1, 2, 3, 4):
+                    try:
+                        m.plan_attention(B, H, S, S, D, dtype=fmt, stages=St, fill=fill)
+                    except m.MgemmError:
+                        continue
+                    m.attention(Q, K, V, O, stages=St, fill=fill)
+                    m.attention(Q, K, V, O1, stages=1, fill="sync")
+                    torch.cuda.synchronize()
+                    if not torch.equal(O.view(torch.int32), O1.view(torch.int32)):
+                        raise SystemExit(f"attention parity gate: {fmt} D{D} {fill} S{St} differs from sync S1")
+                    t = timed_launches(lambda: m.attention(Q, K, V, O, stages=St, fill=fill), repeats=3)
+                    tf = flop / (t["ms_median"] * 1e-3) / 1e12
+                    row[f"{fill}_S{St}"] = {"ms": round(t["ms_median"], 4), "tflops": round(tf, 1),
+                                            "pct_peak": round(100 * tf / PEAK_16BIT_TFLOPS, 2)}
+            t = timed_launches(lambda: F.scaled_dot_product_attention(Q, K, V), repeats=3)
+            row["torch_sdpa_context"] = {"ms": round(t["ms_median"], 4),
+                                         "tflops": round(flop / (t["ms_median"] * 1e-3) / 1e12, 1)}
+            row["best"] = max((k for k in row if k != "torch_sdpa_context"), key=lambda k: row[k]["tflops"])
+            out[f"{fmt}_D{D}"] = row
+            del Q, K, V, O, O1
     return out
 
 
