@@ -345,6 +345,18 @@ struct AttnPipedOps : AttnCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(this->v_ptr(s));
         const int rows = this->rows(s);
         unsigned char *base = this->smem + slot * C::SLOT;
+        if (rows >= kAttnBK) { // a full slice: no masks (a block-uniform branch)
+#pragma unroll
+            for (int i = 0; i < C::OK::U; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_t *)(base + C::OK::lds_off(i, this->wave)), W,
+                                                          this->ok.voff_in(i), 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < C::OV::U; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, (lds_t *)(base + C::LK::BYTES + C::OV::lds_off(i, this->wave)), W, this->ov.voff_in(i), 0, 0,
+                    0);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::OK::U; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_t *)(base + C::OK::lds_off(i, this->wave)), W,
@@ -378,6 +390,15 @@ struct AttnSyncOps : AttnCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(this->k_ptr(s));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(this->v_ptr(s));
         const int rows = this->rows(s);
+        if (rows >= kAttnBK) {
+#pragma unroll
+            for (int i = 0; i < C::OK::U; ++i)
+                vk[SET][i] = ld(rk, this->ok.voff_in(i));
+#pragma unroll
+            for (int i = 0; i < C::OV::U; ++i)
+                vv[SET][i] = ld(rv, this->ov.voff_in(i));
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::OK::U; ++i)
             vk[SET][i] = ld(rk, this->ok.voff(i, rows, C::COLS));

@@ -121,6 +121,8 @@ struct Operand {
     __device__ unsigned voff(int i, int rowlim, int collim) const {
         return (rr[i] < rowlim && cc[i] < collim) ? (unsigned)off[i] * 4u : kMasked;
     }
+    // the offset of a unit known to lie inside the operand (a full slice)
+    __device__ unsigned voff_in(int i) const { return (unsigned)off[i] * 4u; }
 };
 
 // ---- compute tiles ----------------------------------------------------------
@@ -278,6 +280,17 @@ struct MfmaTile {
 
     __device__ void store(float *C, int ldc, int m0, int n0, int M, int N, bool) const {
         const int h = lane >> 5, l32 = lane & 31;
+        if (m0 + BM <= M && n0 + BN <= N) { // interior tile: no bounds per element
+            float *base = C + (size_t)(m0 + 32 * WTM * wm + h * 4) * ldc + n0 + 32 * WTN * wn + l32;
+#pragma unroll
+            for (int ta = 0; ta < WTM; ++ta)
+#pragma unroll
+                for (int tb = 0; tb < WTN; ++tb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        base[(size_t)(32 * ta + (i >> 2) * 8 + (i & 3)) * ldc + 32 * tb] = acc[ta][tb][i];
+            return;
+        }
 #pragma unroll
         for (int ta = 0; ta < WTM; ++ta)
 #pragma unroll
@@ -526,6 +539,17 @@ struct Mfma16Tile {
 
     __device__ void store(float *C, int ldc, int m0, int n0, int M, int N, bool) const {
         const int h = lane >> 5, l32 = lane & 31;
+        if (m0 + BM <= M && n0 + BN <= N) { // interior tile: no bounds per element
+            float *base = C + (size_t)(m0 + 32 * WTM * wm + h * 4) * ldc + n0 + 32 * WTN * wn + l32;
+#pragma unroll
+            for (int ta = 0; ta < WTM; ++ta)
+#pragma unroll
+                for (int tb = 0; tb < WTN; ++tb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        base[(size_t)(32 * ta + (i >> 2) * 8 + (i & 3)) * ldc + 32 * tb] = acc[ta][tb][i];
+            return;
+        }
 #pragma unroll
         for (int ta = 0; ta < WTM; ++ta)
 #pragma unroll
@@ -664,6 +688,12 @@ struct GemmCtx {
     __device__ const float *b_ptr(int s) const { return Bblk + (size_t)s * Tile::B_STEP * ldb; }
     __device__ int a_klim(int s) const { return a_cols - s * Tile::A_STEP; }
     __device__ int b_klim(int s) const { return K - s * Tile::B_STEP; }
+    // every unit of this slice lies inside A and B (the block's rows and
+    // columns and the slice's k range): the loads need no masks (a
+    // block-uniform test, so a scalar branch)
+    __device__ bool full(int ka, int kb) const {
+        return ka >= LA::kCols && kb >= LB::kRows && a_rows >= LA::kRows && b_cols >= LB::kCols;
+    }
     __device__ void barrier() { lds_barrier(); }
     __device__ void compute(int, int slot) {
         const unsigned char *base = smem + slot * SLOT;
@@ -680,6 +710,18 @@ struct PipedOps : GemmCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
         const int ka = this->a_klim(s), kb = this->b_klim(s);
         unsigned char *base = this->smem + slot * C::SLOT;
+        if (this->full(ka, kb)) {
+#pragma unroll
+            for (int i = 0; i < C::OA::U; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t *)(base + C::OA::lds_off(i, this->wave)), W,
+                                                          this->oa.voff_in(i), 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < C::OB::U; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (lds_t *)(base + C::LA::BYTES + C::OB::lds_off(i, this->wave)), W, this->ob.voff_in(i), 0, 0,
+                    0);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::OA::U; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t *)(base + C::OA::lds_off(i, this->wave)), W,
@@ -716,6 +758,15 @@ struct SyncOps : GemmCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
         const int ka = this->a_klim(s), kb = this->b_klim(s);
+        if (this->full(ka, kb)) {
+#pragma unroll
+            for (int i = 0; i < C::OA::U; ++i)
+                va[SET][i] = ld(ra, this->oa.voff_in(i));
+#pragma unroll
+            for (int i = 0; i < C::OB::U; ++i)
+                vb[SET][i] = ld(rb, this->ob.voff_in(i));
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::OA::U; ++i)
             va[SET][i] = ld(ra, this->oa.voff(i, this->a_rows, ka));
