@@ -89,8 +89,8 @@ struct AttnTile {
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x8 __attribute__((ext_vector_type(8)));
 
-    u32x4 qf[NDS];  // this lane's query: elements 16 ds + 8 (l/32) .. +7
-    f32x16 o[NDT];  // O^T tiles (dv tile dt, this wave's 32 queries)
+    u32x4 qf[NDS]; // this lane's query: elements 16 ds + 8 (l/32) .. +7
+    f32x16 o[NDT]; // O^T tiles (dv tile dt, this wave's 32 queries)
     float mrow, lrow, c;
     int lane;
 
@@ -182,6 +182,8 @@ struct AttnTile {
         }
     }
 
+    static constexpr int KT1 = 32 * CPR * 16; // the second 32-key tile, 32 rows on (the swizzle repeats)
+
     // One ring slice: keys key0 .. key0 + 63 of this head (those >= seq_k are
     // masked out; their K and V rows arrive as zeros).
     __device__ void step(const unsigned char *Ks, const unsigned char *Vs, int key0, int seq_k) {
@@ -195,7 +197,6 @@ struct AttnTile {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 s[kt][i] = 0.0f;
-        constexpr int KT1 = 32 * CPR * 16; // the second 32-key tile, 32 rows on (the swizzle repeats)
         u32x4 kf[2][NKT];
         read_k<KT1>(ks + LK::pos(l32, h) * 16, kf[0][0], kf[0][1]);
         wait_k(kf[0][0], kf[0][1]);
@@ -345,7 +346,7 @@ struct AttnPipedOps : AttnCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(this->v_ptr(s));
         const int rows = this->rows(s);
         unsigned char *base = this->smem + slot * C::SLOT;
-        if (rows >= kAttnBK) { // a full slice: no masks (a block-uniform branch)
+        if (__builtin_expect(rows >= kAttnBK, 1)) { // a full slice: no masks (a block-uniform branch)
 #pragma unroll
             for (int i = 0; i < C::OK::U; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_t *)(base + C::OK::lds_off(i, this->wave)), W,
@@ -390,7 +391,7 @@ struct AttnSyncOps : AttnCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(this->k_ptr(s));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(this->v_ptr(s));
         const int rows = this->rows(s);
-        if (rows >= kAttnBK) {
+        if (__builtin_expect(rows >= kAttnBK, 1)) {
 #pragma unroll
             for (int i = 0; i < C::OK::U; ++i)
                 vk[SET][i] = ld(rk, this->ok.voff_in(i));

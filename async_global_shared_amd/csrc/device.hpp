@@ -94,24 +94,30 @@ struct Operand {
     static constexpr int U = (W == 16) ? L::CHUNKS / (64 * WAVES) : (L::CHUNKS * 4) / (64 * WAVES);
     static_assert(W == 16 || W == 4, "load width");
     static_assert(L::CHUNKS % (64 * WAVES) == 0, "whole wave instructions per slice");
-    int rr[U], cc[U], off[U];
+    // only the element offsets stay in registers; a unit's row and column are
+    // recomputed (shifts and masks) where an edge slice needs them
+    int off[U];
+    int lane, wave;
 
-    __device__ void init(int lane, int wave, int ld) {
+    __device__ void rc(int i, int &r, int &c) const {
+        const int g = i * WAVES + wave;
+        if constexpr (W == 16) {
+            const int p = g * 64 + lane;
+            r = L::row(p);
+            c = 4 * L::col4(p);
+        } else {
+            const int q = g * 64 + lane;
+            r = L::row(q >> 2);
+            c = 4 * L::col4(q >> 2) + (q & 3);
+        }
+    }
+    __device__ void init(int lane_, int wave_, int ld) {
+        lane = lane_;
+        wave = wave_;
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const int g = i * WAVES + wave;
             int r, c;
-            if constexpr (W == 16) {
-                const int p = g * 64 + lane;
-                r = L::row(p);
-                c = 4 * L::col4(p);
-            } else {
-                const int q = g * 64 + lane;
-                r = L::row(q >> 2);
-                c = 4 * L::col4(q >> 2) + (q & 3);
-            }
-            rr[i] = r;
-            cc[i] = c;
+            rc(i, r, c);
             off[i] = r * ld + c;
         }
     }
@@ -119,7 +125,9 @@ struct Operand {
     __device__ static constexpr int lds_off(int i, int wave) { return (i * WAVES + wave) * 64 * W; }
 
     __device__ unsigned voff(int i, int rowlim, int collim) const {
-        return (rr[i] < rowlim && cc[i] < collim) ? (unsigned)off[i] * 4u : kMasked;
+        int r, c;
+        rc(i, r, c);
+        return (r < rowlim && c < collim) ? (unsigned)off[i] * 4u : kMasked;
     }
     // the offset of a unit known to lie inside the operand (a full slice)
     __device__ unsigned voff_in(int i) const { return (unsigned)off[i] * 4u; }
@@ -464,19 +472,22 @@ struct Mfma16Tile {
     // The k steps of a slice are software-pipelined: step ks+1's reads are
     // in flight while step ks's MFMAs run (scheduling barriers keep the
     // MFMAs between the issue and the wait).
-    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
-        static_assert(WTN == 2 && (WTM == 2 || WTM == 4), "issue_reads covers these wave tiles");
-        const int h = lane >> 5, l32 = lane & 31, q = lane & 15, g16 = (lane >> 4) & 1;
-        const unsigned as = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)As;
+    __device__ void lane_addrs(const unsigned char *As, const unsigned char *Bs, unsigned &as, unsigned *ab) const {
+        const int h = lane >> 5, q = lane & 15, g16 = (lane >> 4) & 1;
+        as = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)As;
         const unsigned bs = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)Bs;
-        const int m = 32 * WTM * wm + l32;
-        unsigned ab[WTN];
 #pragma unroll
         for (int tb = 0; tb < WTN; ++tb) {
             const int k = 8 * h + (q >> 2);
             const int n = 32 * WTN * wn + 32 * tb + 16 * g16 + 4 * (q & 3);
             ab[tb] = bs + LB::pos(k, n >> 3) * 16 + (n & 7) * 2;
         }
+    }
+    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
+        static_assert(WTN == 2 && (WTM == 2 || WTM == 4), "issue_reads covers these wave tiles");
+        const int h = lane >> 5, m = 32 * WTM * wm + (lane & 31);
+        unsigned as, ab[WTN];
+        lane_addrs(As, Bs, as, ab);
         constexpr int NKS = KPS / 16;
         Frag f[2];
         issue_reads<0>(as + LA::pos(m, h) * 16, ab, f[0]);
@@ -642,6 +653,18 @@ __device__ inline void wait_vm() {
 // Block barrier after this wave's LDS reads and writes have completed.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// The full-slice branch of the fills is hinted as the likely one for 16-byte
+// loads (the common layout; measured faster on the 4096^3 three-stage ring).
+// The 4-byte loaders of the big 16-bit tiles get no hint: with it, their
+// register allocation spills.
+template <int W>
+__device__ inline bool likely_full(bool full) {
+    if constexpr (W == 16)
+        return __builtin_expect(full, 1);
+    else
+        return full;
+}
+
 // A and B are addressed as 32-bit words (fp32 elements, or pairs of 16-bit
 // elements); lda and ldb are in words, a_cols is the row extent of A in words.
 struct GemmArgs {
@@ -710,7 +733,7 @@ struct PipedOps : GemmCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
         const int ka = this->a_klim(s), kb = this->b_klim(s);
         unsigned char *base = this->smem + slot * C::SLOT;
-        if (this->full(ka, kb)) {
+        if (likely_full<W>(this->full(ka, kb))) {
 #pragma unroll
             for (int i = 0; i < C::OA::U; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t *)(base + C::OA::lds_off(i, this->wave)), W,
@@ -758,7 +781,7 @@ struct SyncOps : GemmCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
         const int ka = this->a_klim(s), kb = this->b_klim(s);
-        if (this->full(ka, kb)) {
+        if (likely_full<W>(this->full(ka, kb))) {
 #pragma unroll
             for (int i = 0; i < C::OA::U; ++i)
                 va[SET][i] = ld(ra, this->oa.voff_in(i));

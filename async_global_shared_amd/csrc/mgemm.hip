@@ -292,10 +292,11 @@ int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
     const bool b128_ok = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 && N % 8 == 0;
     const int W = b128_ok ? 16 : 4;
     if (tile == MGEMM_TILE_AUTO)
-        // the largest tile that still gives every CU a block (measured at 4096^3 and 8192^3)
-        tile = ((M + 255) / 256) * ((N + 255) / 256) >= 256   ? MGEMM_TILE_256x256
-               : ((M + 255) / 256) * ((N + 127) / 128) >= 512 ? MGEMM_TILE_256x128
-                                                                : MGEMM_TILE_128x128;
+        // the largest tile that still gives every CU a block (measured at 4096^3 and 8192^3);
+        // with 4-byte loads the 8-wave tile would spill (every wave holds 256 VGPRs at most)
+        tile = (W == 16 && ((M + 255) / 256) * ((N + 255) / 256) >= 256) ? MGEMM_TILE_256x256
+               : ((M + 255) / 256) * ((N + 127) / 128) >= 512           ? MGEMM_TILE_256x128
+                                                                          : MGEMM_TILE_128x128;
     const int bm = tile == MGEMM_TILE_128x128 ? 128 : 256, bn = tile == MGEMM_TILE_256x256 ? 256 : 128;
     const int waves = tile == MGEMM_TILE_256x256 ? 8 : kWaves;
     constexpr int kps = kK16;

@@ -509,6 +509,9 @@ def test_gemm16_plans():
     assert p["load_bytes"] == 4 and p["slices"] == 4 and p["loads_per_slice"] == 32 and p["max_vmcnt"] == 32
     assert m.plan16(300, 264, 200, lda=208, ldb=272)["load_bytes"] == 16
     assert m.plan16(64, 64, 64, a_ptr=0x10004)["load_bytes"] == 4
+    # misaligned big problems keep 4-byte loads and the 4-wave 256 x 128 tile
+    p = m.plan16(8192, 8192, 8192, a_ptr=0x10004)
+    assert (p["load_bytes"], p["bm"], p["bn"]) == (4, 256, 128)
 
 
 def _name16(cfg, bf16, S, piped, W):
@@ -566,24 +569,36 @@ def _regs(operand):
 
 
 def _early_uses_of_lds_results(lines):
-    """Instructions that read or overwrite the destination of an LDS read
-    before an s_waitcnt lgkmcnt(0) (in layout order): the wait the LDS
-    reads issued from inline asm depend on."""
-    pending, bad = set(), []
-    for raw in lines:
-        ins = raw.split(";")[0].strip()
-        if not ins or ins.startswith(".") or ins.endswith(":"):
-            continue
-        op, _, rest = ins.partition(" ")
-        ops = [o.strip() for o in rest.split(",")]
-        if op == "s_waitcnt" and "lgkmcnt(0)" in rest:
-            pending.clear()
-            continue
-        used = set().union(*(_regs(o.split()[0]) for o in ops if o)) if ops else set()
-        if used & pending:
-            bad.append(ins)
-        if op.startswith("ds_read"):
-            pending |= _regs(ops[0])
+    """Instructions that read or overwrite the destination of an LDS read on
+    some control-flow path before an s_waitcnt lgkmcnt(0): the wait the LDS
+    reads issued from inline asm depend on. A forward may-analysis over the
+    basic blocks of `_cfg` (pending registers join at block entries)."""
+    blocks = _cfg(lines)
+    index = {lab: i for i, (lab, _, _) in enumerate(blocks)}
+    entry = {0: frozenset()}
+    work, bad = [0], []
+    while work:
+        i = work.pop()
+        pending = set(entry[i])
+        for ins in blocks[i][1]:
+            op, _, rest = ins.partition(" ")
+            ops = [o.strip() for o in rest.split(",")]
+            if op == "s_waitcnt" and "lgkmcnt(0)" in rest:
+                pending.clear()
+                continue
+            used = set().union(*(_regs(o.split()[0]) for o in ops if o)) if ops else set()
+            if used & pending and ins not in bad:
+                bad.append(ins)
+            if op.startswith("ds_read"):
+                pending |= _regs(ops[0])
+        for succ in blocks[i][2]:
+            j = index.get(succ)
+            if j is None:
+                continue
+            new = frozenset(pending) | entry.get(j, frozenset())
+            if j not in entry or new != entry[j]:
+                entry[j] = new
+                work.append(j)
     return bad
 
 
@@ -591,6 +606,14 @@ def test_isa_guard_sees_an_early_use():
     lines = ["ds_read_b128 v[4:7], v1", "v_mov_b32_e32 v9, v5", "s_waitcnt lgkmcnt(0)", "v_mov_b32_e32 v9, v5"]
     assert _early_uses_of_lds_results(lines) == ["v_mov_b32_e32 v9, v5"]
     assert _early_uses_of_lds_results(lines[:1] + lines[2:]) == []
+    # a use reached only over a branch that skips the wait is caught ...
+    lines = ["ds_read_b128 v[4:7], v1", "s_cbranch_scc1 .LBB0_2", "s_waitcnt lgkmcnt(0)", ".LBB0_2:",
+             "v_mov_b32_e32 v9, v6", "s_endpgm"]
+    assert _early_uses_of_lds_results(lines) == ["v_mov_b32_e32 v9, v6"]
+    # ... and code laid out after an unconditional branch is not on the read's path
+    lines = [".LBB0_1:", "s_waitcnt lgkmcnt(0)", "ds_read_b128 v[4:7], v1", "s_branch .LBB0_1",
+             ".LBB0_3:", "v_mov_b32_e32 v9, v6", "s_endpgm"]
+    assert _early_uses_of_lds_results(lines) == []
 
 
 @pytest.mark.parametrize("cfg", H16_CFGS)
@@ -694,3 +717,33 @@ def test_isa_attention(isa, D):
                         assert "ds_write" in body and not re.search(r"buffer_load\S* .* lds", body)
                     assert not _early_uses_of_lds_results(lines), (D, bf16, S, W, piped)
                     assert "v_pk_fma_f32" not in body and "v_pk_add_f32" not in body and "v_pk_mul_f32" not in body
+
+
+def test_isa_no_kernel_spills():
+    """No kernel spills registers to scratch: a scratch reload would count in
+    vmcnt, and the compiler would then drain the in-flight fills before it.
+    Documented exceptions, none ever chosen automatically: the
+    warp-specialised ring with the 8 x 8 VALU tile (512-thread blocks cap
+    every wave at 256 registers, which that tile and both roles' state
+    exceed); the register-staged 16-bit rings of the 256-row tiles with
+    4-byte loads (a slice's 32 single-dword loads per register set beside 128
+    accumulators), which only misaligned inputs with an explicit synchronous
+    fill reach; and the 8-wave 256 x 256 tile with 4-byte loads at two stages
+    (three dwords over the 256-VGPR cap of 512-thread blocks), which only an
+    explicit tile request with misaligned inputs reaches."""
+    if not os.path.exists(m.ISA_PATH):
+        pytest.skip("ISA not built")
+    txt = open(m.ISA_PATH).read()
+    sizes = re.findall(r"^(_ZN5mgemm\w+):.*?; ScratchSize: (\d+)", txt, re.M | re.S)
+    names = re.findall(r"^(_ZN5mgemm\w+):", txt, re.M)
+    assert len(names) >= 200
+    spilled = []
+    for name in names:
+        i = txt.index("; Kernel info:", txt.index(name + ":"))
+        size = int(re.search(r"; ScratchSize: (\d+)", txt[i:i + 600]).group(1))
+        allowed = name.startswith("_ZN5mgemm15sgemm_ws_kernelINS_10CfgValu128E") or \
+            re.fullmatch(r"_ZN5mgemm12sgemm_kernelINS_\d+CfgH256x(128|256)ILb[01]EEELi[23]ELb0ELi4EEEvNS_8GemmArgsE", name) or \
+            re.fullmatch(r"_ZN5mgemm12sgemm_kernelINS_11CfgH256x256ILb[01]EEELi2ELb1ELi4EEEvNS_8GemmArgsE", name)
+        if size and not allowed:
+            spilled.append((name, size))
+    assert not spilled, spilled[:5]
