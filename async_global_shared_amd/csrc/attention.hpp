@@ -8,7 +8,7 @@
 // softmax). The ring, its loaders and its waits are the GEMM's; only the
 // per-slice step differs.
 //
-// Per block 4 waves x 32 queries of one (batch, head); per slice 64 keys.
+// Per block 8 waves x 32 queries of one (batch, head); per slice 64 keys.
 // Each wave works in the transposed form so that a lane owns one query:
 //   S^T (64 keys x 32 queries) = K (from LDS) . Q^T (registers, loaded once)
 //   O^T (D x 32 queries)      += V^T (transposing LDS reads) . P^T
@@ -24,7 +24,7 @@
 namespace mgemm {
 
 constexpr int kAttnBK = 64;                 // keys per ring slice
-constexpr int kAttnWaves = 4;               // waves per block, 32 queries each
+constexpr int kAttnWaves = 8;               // waves per block (2 per SIMD), 32 queries each
 constexpr int kAttnBQ = 32 * kAttnWaves;    // queries per block
 constexpr int kAttnThreads = 64 * kAttnWaves;
 

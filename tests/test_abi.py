@@ -672,13 +672,13 @@ def test_attention_rejects_nonfinite_scale():
 
 def test_attention_plans():
     p = m.plan_attention(16, 16, 4096, 4096, 128)
-    assert (p["bm"], p["bn"], p["bk"], p["threads"], p["blocks"]) == (128, 128, 64, 256, 16 * 16 * 32)
+    assert (p["bm"], p["bn"], p["bk"], p["threads"], p["blocks"]) == (256, 128, 64, 512, 16 * 16 * 16)
     assert p["slices"] == 64 and p["load_bytes"] == 16 and p["lds_bytes"] == 2 * 2 * 64 * 128 * 2
-    # one slice: a 64 x 128 K tile and a V tile, 32 KiB = 8 dwordx4 per lane of each of 4 waves
-    assert p["loads_per_slice"] == 8 and p["max_vmcnt"] == 0
-    assert m.plan_attention(16, 16, 4096, 4096, 128, stages=4)["max_vmcnt"] == 16
+    # one slice: a 64 x 128 K tile and a V tile, 32 KiB = 4 dwordx4 per lane of each of 8 waves
+    assert p["loads_per_slice"] == 4 and p["max_vmcnt"] == 0
+    assert m.plan_attention(16, 16, 4096, 4096, 128, stages=4)["max_vmcnt"] == 8
     p = m.plan_attention(1, 3, 200, 300, 64, stages=3, fill="sync", align=4)
-    assert p["load_bytes"] == 4 and p["blocks"] == 3 * 2 and p["slices"] == 5 and p["loads_per_slice"] == 16
+    assert p["load_bytes"] == 4 and p["blocks"] == 3 * 1 and p["slices"] == 5 and p["loads_per_slice"] == 8
     # the (batch, seq, head, dim) layout keeps 16-byte loads when its strides allow
     st, p = att(B=2, H=4, Sq=64, Sk=64, D=128, q=(64 * 4 * 128, 128, 4 * 128), k=(64 * 4 * 128, 128, 4 * 128),
                 v=(64 * 4 * 128, 128, 4 * 128))
