@@ -154,11 +154,14 @@ struct AttnTile {
             return __builtin_bit_cast(u32x4, __builtin_convertvector(p, f16x8));
     }
 
-    // Load this lane's query row (zero beyond seq_q) and clear the state.
+    // Load this lane's query row (zero beyond seq_q) and clear the state. A
+    // negative scale is folded into the sign of Q (every 16-bit element's
+    // sign bit flipped: the MFMA then forms exactly -s, as its products and
+    // round-to-nearest sums are sign-symmetric), so that c >= 0.
     template <int W>
     __device__ void init(int tid, const float *Qh, int q_ld, int row, int seq_q, float c_) {
         lane = tid & 63;
-        c = c_;
+        c = c_ < 0.0f ? -c_ : c_;
         mrow = -__builtin_inff();
         lrow = 0.0f;
 #pragma unroll
@@ -180,9 +183,55 @@ struct AttnTile {
                     qf[ds][j] = __builtin_amdgcn_raw_buffer_load_b32(r, row < seq_q ? off + 4 * j : kMasked, 0, 0);
             }
         }
+        if (c_ < 0.0f) { // block-uniform
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds)
+                qf[ds] ^= 0x80008000u;
+        }
     }
 
     static constexpr int KT1 = 32 * CPR * 16; // the second 32-key tile, 32 rows on (the swizzle repeats)
+
+    // Online softmax over one slice's scores s (replaced by the
+    // probabilities). x = c s with c = scale log2(e) >= 0 (init() folds a
+    // negative scale into the sign of Q); p = 2^(x - m) is formed as one fma,
+    // 2^(fma(s, c, -m)), with m the running maximum of x, c times the raw
+    // maximum. Keys >= seq_k (FULL false: the last slice) get p = 0. O is
+    // rescaled unless every lane's maximum stayed put (alpha == 1 exactly:
+    // x * 1 == x, so skipping changes no bit).
+    template <bool FULL>
+    __device__ void softmax(f32x16 (&s)[NKT], int key0, int seq_k) {
+        const int h = lane >> 5;
+        auto valid = [&](int kt, int i) { return key0 + 32 * kt + 8 * (i >> 2) + 4 * h + (i & 3) < seq_k; };
+        float ext = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                ext = fmaxf(ext, FULL || valid(kt, i) ? s[kt][i] : -__builtin_inff());
+        const float mnew = fmaxf(mrow, c * pair_max(ext)); // finite: key0 < seq_k
+        const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+        float rs = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c, -mnew));
+                if constexpr (!FULL)
+                    p = valid(kt, i) ? p : 0.0f;
+                s[kt][i] = p;
+                rs += p;
+            }
+        lrow = lrow * alpha + pair_sum(rs);
+        mrow = mnew;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    o[dt][i] *= alpha;
+        }
+    }
 
     // One ring slice: keys key0 .. key0 + 63 of this head (those >= seq_k are
     // masked out; their K and V rows arrive as zeros).
@@ -214,34 +263,12 @@ struct AttnTile {
         });
 
         // ---- online softmax (log2 domain) ----
-        float mloc = -__builtin_inff();
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * h + (i & 3);
-                const float x = key < seq_k ? s[kt][i] * c : -__builtin_inff();
-                s[kt][i] = x;
-                mloc = fmaxf(mloc, x);
-            }
-        const float mnew = fmaxf(mrow, pair_max(mloc)); // finite: key0 < seq_k
-        const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
-        float rs = 0.0f;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(s[kt][i] - mnew);
-                s[kt][i] = p;
-                rs += p;
-            }
-        lrow = lrow * alpha + pair_sum(rs);
-        mrow = mnew;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                o[dt][i] *= alpha;
+        // only the last slice can hold keys >= seq_k (a block-uniform test);
+        // at head dim 64 one masked copy keeps the registers for 4 waves per SIMD
+        if (D == 128 && key0 + BK <= seq_k)
+            softmax<true>(s, key0, seq_k);
+        else
+            softmax<false>(s, key0, seq_k);
 
         // ---- O^T += V^T P^T, 16-key steps pipelined one ahead ----
         u32x4 pf[NKK];
@@ -419,12 +446,13 @@ struct AttnSyncOps : AttnCtx<Tile, W> {
     }
 };
 
-#ifndef MGEMM_ATTN_WAVES_PER_EU
-#define MGEMM_ATTN_WAVES_PER_EU 2 // two waves per SIMD: one wave's softmax overlaps the other's MFMAs
-#endif
+// Two waves per SIMD at least: one wave's softmax overlaps the other's MFMAs.
+template <int D>
+constexpr int kAttnWavesPerEu = 2;
+
 template <int D, bool BF16, int S, bool PIPED, int W>
 __global__ void __launch_bounds__(kAttnThreads)
-    __attribute__((amdgpu_waves_per_eu(MGEMM_ATTN_WAVES_PER_EU))) attention_kernel(AttnArgs a) {
+    __attribute__((amdgpu_waves_per_eu(kAttnWavesPerEu<D>))) attention_kernel(AttnArgs a) {
     using Tile = AttnTile<D, BF16>;
     using Ctx = AttnCtx<Tile, W>;
     constexpr bool kFits = S * Ctx::SLOT <= kLdsBytes;

@@ -126,10 +126,11 @@ def test_layouts(fmt):
             assert bool(torch.all(buf[..., D:] == SENTINEL))
 
 
-@pytest.mark.parametrize("scale", [0.0, 2.0, 40.0])
+@pytest.mark.parametrize("scale", [0.0, 2.0, 40.0, -1.5])
 def test_scales(scale):
     """scale 0 (uniform weights: the mean of V), peaked and nearly one-hot
-    softmax rows."""
+    softmax rows, and a negative scale (the row maximum of scale * s is then
+    scale * min(s))."""
     fmt, B, H, Sq, Sk, D = "bf16", 1, 2, 96, 200, 64
     Q, K, V = (dev_qkv(s, B, H, n, D, fmt) for s, n in ((7, Sq), (8, Sk), (9, Sk)))
     O = m.attention(Q, K, V, scale=scale)
