@@ -417,32 +417,34 @@ struct Mfma16Tile {
         constexpr int TA = 32 * LA::CPR * 16;
         constexpr int B0 = (16 * KS) * LB::CPR * 16, B1 = (16 * KS + 4) * LB::CPR * 16;
         if constexpr (WTM == 4)
-            asm volatile("ds_read_b128 %0, %8\n\t"
-                         "ds_read_b128 %1, %8 offset:%11\n\t"
-                         "ds_read_b128 %2, %8 offset:%12\n\t"
-                         "ds_read_b128 %3, %8 offset:%13\n\t"
-                         "ds_read_b64_tr_b16 %4, %9 offset:%14\n\t"
-                         "ds_read_b64_tr_b16 %5, %9 offset:%15\n\t"
-                         "ds_read_b64_tr_b16 %6, %10 offset:%14\n\t"
-                         "ds_read_b64_tr_b16 %7, %10 offset:%15"
-                         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3]), "=&v"(f.b[0][0]),
-                           "=&v"(f.b[0][1]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1])
-                         : "v"(aa), "v"(ab[0]), "v"(ab[1]), "i"(TA), "i"(2 * TA), "i"(3 * TA), "i"(B0), "i"(B1));
+            asm volatile("ds_read_b128 %0, %4\n\t"
+                         "ds_read_b128 %1, %4 offset:%5\n\t"
+                         "ds_read_b128 %2, %4 offset:%6\n\t"
+                         "ds_read_b128 %3, %4 offset:%7"
+                         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.a[2]), "=&v"(f.a[3])
+                         : "v"(aa), "i"(TA), "i"(2 * TA), "i"(3 * TA));
         else
-            asm volatile("ds_read_b128 %0, %6\n\t"
-                         "ds_read_b128 %1, %6 offset:%9\n\t"
-                         "ds_read_b64_tr_b16 %2, %7 offset:%10\n\t"
-                         "ds_read_b64_tr_b16 %3, %7 offset:%11\n\t"
-                         "ds_read_b64_tr_b16 %4, %8 offset:%10\n\t"
-                         "ds_read_b64_tr_b16 %5, %8 offset:%11"
-                         : "=&v"(f.a[0]), "=&v"(f.a[1]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]), "=&v"(f.b[1][0]),
-                           "=&v"(f.b[1][1])
-                         : "v"(aa), "v"(ab[0]), "v"(ab[1]), "i"(TA), "i"(B0), "i"(B1));
+            asm volatile("ds_read_b128 %0, %2\n\t"
+                         "ds_read_b128 %1, %2 offset:%3"
+                         : "=&v"(f.a[0]), "=&v"(f.a[1])
+                         : "v"(aa), "i"(TA));
+        // two transposing reads (row quads 0 and 1) per column tile
+#pragma unroll
+        for (int tb = 0; tb < WTN; ++tb)
+            asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+                         "ds_read_b64_tr_b16 %1, %2 offset:%4"
+                         : "=&v"(f.b[tb][0]), "=&v"(f.b[tb][1])
+                         : "v"(ab[tb]), "i"(B0), "i"(B1));
     }
     // Wait for every LDS read of this wave; the fragment's registers are
     // outputs of the wait, so nothing reads them before it.
     __device__ static void wait_reads(Frag &f) {
-        if constexpr (WTM == 4)
+        if constexpr (WTM == 4 && WTN == 4)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0][0]), "+v"(f.b[0][1]),
+                           "+v"(f.b[1][0]), "+v"(f.b[1][1]), "+v"(f.b[2][0]), "+v"(f.b[2][1]), "+v"(f.b[3][0]),
+                           "+v"(f.b[3][1]));
+        else if constexpr (WTM == 4)
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0][0]), "+v"(f.b[0][1]),
                            "+v"(f.b[1][0]), "+v"(f.b[1][1]));
@@ -451,27 +453,30 @@ struct Mfma16Tile {
                          : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.b[0][0]), "+v"(f.b[0][1]), "+v"(f.b[1][0]),
                            "+v"(f.b[1][1]));
     }
+    template <int ta, int tb>
+    __device__ void mfma_one(const Frag &f) {
+        const i16x4 lo = f.b[tb][0], hi = f.b[tb][1];
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (BF16)
+            acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, f.a[ta]), __builtin_bit_cast(bf16x8, bv), acc[ta][tb], 0, 0, 0);
+        else
+            acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, f.a[ta]), __builtin_bit_cast(f16x8, bv), acc[ta][tb], 0, 0, 0);
+    }
     __device__ void mfma(const Frag &f) {
-#pragma unroll
-        for (int ta = 0; ta < WTM; ++ta)
-#pragma unroll
-            for (int tb = 0; tb < WTN; ++tb) {
-                const i16x4 lo = f.b[tb][0], hi = f.b[tb][1];
-                typedef short i16x8 __attribute__((ext_vector_type(8)));
-                const i16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                if constexpr (BF16)
-                    acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, f.a[ta]), __builtin_bit_cast(bf16x8, bv), acc[ta][tb], 0, 0, 0);
-                else
-                    acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(f16x8, f.a[ta]), __builtin_bit_cast(f16x8, bv), acc[ta][tb], 0, 0, 0);
-            }
+        static_for<0, WTM * WTN>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            mfma_one<j / WTN, j % WTN>(f);
+        });
     }
 
 #if MGEMM_H16_PIPE
-    // The k steps of a slice are software-pipelined: step ks+1's reads are
-    // in flight while step ks's MFMAs run (scheduling barriers keep the
-    // MFMAs between the issue and the wait).
+#ifndef MGEMM_H16_SPLIT
+#define MGEMM_H16_SPLIT 1
+#endif
+    static constexpr bool kSplit = MGEMM_H16_SPLIT;
     __device__ void lane_addrs(const unsigned char *As, const unsigned char *Bs, unsigned &as, unsigned *ab) const {
         const int h = lane >> 5, q = lane & 15, g16 = (lane >> 4) & 1;
         as = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)As;
@@ -483,25 +488,66 @@ struct Mfma16Tile {
             ab[tb] = bs + LB::pos(k, n >> 3) * 16 + (n & 7) * 2;
         }
     }
-    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
-        static_assert(WTN == 2 && (WTM == 2 || WTM == 4), "issue_reads covers these wave tiles");
+    // The k steps of a slice are software-pipelined: step ks+1's reads are
+    // in flight while step ks's MFMAs run (scheduling barriers keep the
+    // MFMAs between the issue and the wait). head, body and tail split one
+    // slice's compute at its ends (the split ring interleaves them across
+    // slices); compute runs the three in a row.
+    static constexpr int NKS = KPS / 16;
+    static_assert(NKS % 2 == 0, "the last k step's fragment set differs from the first's");
+    Frag fr[2];
+    __device__ void head(const unsigned char *As, const unsigned char *Bs) {
+        static_assert((WTN == 2 && (WTM == 2 || WTM == 4)) || (WTN == 4 && WTM == 4), "wait_reads covers these wave tiles");
         const int h = lane >> 5, m = 32 * WTM * wm + (lane & 31);
         unsigned as, ab[WTN];
         lane_addrs(As, Bs, as, ab);
-        constexpr int NKS = KPS / 16;
-        Frag f[2];
-        issue_reads<0>(as + LA::pos(m, h) * 16, ab, f[0]);
-        wait_reads(f[0]);
-        static_for<0, NKS>([&](auto ksc) {
+        issue_reads<0>(as + LA::pos(m, h) * 16, ab, fr[0]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __device__ void body(const unsigned char *As, const unsigned char *Bs) {
+        const int h = lane >> 5, m = 32 * WTM * wm + (lane & 31);
+        unsigned as, ab[WTN];
+        lane_addrs(As, Bs, as, ab);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_reads(fr[0]);
+        static_for<0, NKS - 1>([&](auto ksc) {
             constexpr int ks = decltype(ksc)::value;
-            if constexpr (ks + 1 < NKS)
-                issue_reads<ks + 1>(as + LA::pos(m, 2 * (ks + 1) + h) * 16, ab, f[(ks + 1) & 1]);
+            issue_reads<ks + 1>(as + LA::pos(m, 2 * (ks + 1) + h) * 16, ab, fr[(ks + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            mfma(f[ks & 1]);
+            mfma(fr[ks & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (ks + 1 < NKS)
-                wait_reads(f[(ks + 1) & 1]);
+            wait_reads(fr[(ks + 1) & 1]);
         });
+    }
+    __device__ void tail() {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(fr[(NKS - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // The same MFMAs with f(Int<j>) placed after the j-th of them (the ring
+    // spreads a slice's fill instructions there, so no wave stalls on a
+    // burst of them while the matrix pipe runs dry).
+    static constexpr int TAIL_OPS = WTM * WTN;
+    // Spread the ring's refill over the tail: measured faster for the 8-wave
+    // tile (two waves per SIMD stall together on a burst of fills); the
+    // 4-wave tiles hold twice the fill units per wave, and keeping their
+    // offsets live across the tail costs them occupancy.
+    static constexpr bool kSpreadFill = WAVES == 8;
+    template <class F>
+    __device__ void tail_with(F &&f) {
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, TAIL_OPS>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            mfma_one<j / WTN, j % WTN>(fr[(NKS - 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            f(jc);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
+        head(As, Bs);
+        body(As, Bs);
+        tail();
     }
 #else
     __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
@@ -610,8 +656,12 @@ struct CfgH256x128 {
     static constexpr int BM = 256, BN = 128;
 };
 template <bool BF16>
+#ifndef MGEMM_H256_WAVES
+#define MGEMM_H256_WAVES 8
+#endif
 struct CfgH256x256 { // 8 waves (2 per SIMD), each 128 x 64 as in the 256 x 128 tile
-    using Tile = Mfma16Tile<4, 2, 2, 4, BF16>;
+    using Tile = typename std::conditional<MGEMM_H256_WAVES == 8, Mfma16Tile<4, 2, 2, 4, BF16>,
+                                           Mfma16Tile<4, 4, 2, 2, BF16>>::type;
     static constexpr int BM = 256, BN = 256;
 };
 
@@ -653,6 +703,17 @@ __device__ inline void wait_vm() {
 // Block barrier after this wave's LDS reads and writes have completed.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// One asynchronous global -> LDS fill instruction of W bytes per lane. (The
+// width is spelled as a literal: clang checks this builtin's size argument
+// before a function template is instantiated.)
+template <int W>
+__device__ inline void lds_dma(__amdgpu_buffer_rsrc_t r, unsigned char *lds, unsigned off) {
+    if constexpr (W == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t *)lds, 16, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t *)lds, 4, off, 0, 0, 0);
+}
+
 // The full-slice branch of the fills is hinted as the likely one for 16-byte
 // loads (the common layout; measured faster on the 4096^3 three-stage ring).
 // The 4-byte loaders of the big 16-bit tiles get no hint: with it, their
@@ -686,6 +747,13 @@ template <>
 struct RegOf<4> {
     using type = unsigned;
 };
+
+// Tiles whose compute splits into head / body / tail run the split ring
+// (with 16-byte loads).
+template <class T, class = void>
+struct SplitTile : std::false_type {};
+template <class T>
+struct SplitTile<T, std::void_t<decltype(T::kSplit)>> : std::integral_constant<bool, T::kSplit> {};
 
 // State one block of the GEMM shares between its ring operations.
 template <class Tile, int W>
@@ -722,38 +790,102 @@ struct GemmCtx {
         const unsigned char *base = smem + slot * SLOT;
         tile.compute(base, base + LA::BYTES);
     }
+    // the split ring's three parts (tiles with head / body / tail)
+    __device__ void head(int, int slot) {
+        const unsigned char *base = smem + slot * SLOT;
+        tile.head(base, base + LA::BYTES);
+    }
+    __device__ void body(int, int slot) {
+        const unsigned char *base = smem + slot * SLOT;
+        tile.body(base, base + LA::BYTES);
+    }
+    __device__ void tail(int) { tile.tail(); }
 };
 
 // Asynchronous fill: buffer_load ... lds straight into the ring slot.
 template <class Tile, int W>
 struct PipedOps : GemmCtx<Tile, W> {
     using C = GemmCtx<Tile, W>;
+    static constexpr int UNITS = C::OA::U + C::OB::U;
+    // Slice s's fill instructions one unit at a time (units 0 .. OA::U-1 are
+    // A's, the rest B's; FULL: the slice lies inside A and B). The buffer
+    // resources are sizeless, so they travel as arguments, not in a struct.
+    template <int u, bool FULL>
+    __device__ void unit(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, unsigned char *base, int ka, int kb) {
+        if constexpr (u < C::OA::U) {
+            const unsigned off = FULL ? this->oa.voff_in(u) : this->oa.voff(u, this->a_rows, ka);
+            lds_dma<W>(ra, base + C::OA::lds_off(u, this->wave), off);
+        } else {
+            constexpr int i = u - C::OA::U;
+            const unsigned off = FULL ? this->ob.voff_in(i) : this->ob.voff(i, kb, this->b_cols);
+            lds_dma<W>(rb, base + C::LA::BYTES + C::OB::lds_off(i, this->wave), off);
+        }
+    }
+    template <int B, int E, bool FULL>
+    __device__ void units(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, unsigned char *base, int ka, int kb) {
+        static_for<B, E>([&](auto uc) { this->template unit<decltype(uc)::value, FULL>(ra, rb, base, ka, kb); });
+    }
     __device__ void issue(int s, int slot) {
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s));
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s)), rb = make_rsrc(this->b_ptr(s));
         const int ka = this->a_klim(s), kb = this->b_klim(s);
         unsigned char *base = this->smem + slot * C::SLOT;
-        if (likely_full<W>(this->full(ka, kb))) {
+        if (likely_full<W>(this->full(ka, kb)))
+            units<0, UNITS, true>(ra, rb, base, ka, kb);
+        else
+            units<0, UNITS, false>(ra, rb, base, ka, kb);
+    }
+    // tail(slice - 1) of the split ring with issue(s, slot) spread over its
+    // MFMAs: the j-th MFMA is followed by units [j U / J, (j + 1) U / J).
+    // Only the offsets depend on the full-slice test; the MFMAs stay out of
+    // that branch, or each side would get its own accumulator registers.
+    // Without `refill` (the last S-1 slices) only the tail runs; the test is
+    // block-uniform and guards the fill instructions alone. (16-byte loaders
+    // only: the 4-byte ones, with four times the units, keep the plain ring.)
+    // Tiles without kSpreadFill issue the slice before the tail instead:
+    // the offsets held across the tail would cost them occupancy.
+    __device__ void tail_issue(int tprev, int s, int slot, bool refill) {
+        static_assert(W == 16, "the split ring runs with 16-byte loads");
+        if constexpr (!Tile::kSpreadFill) {
+            if (refill)
+                issue(s, slot);
+            this->tail(tprev);
+        } else {
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s)), rb = make_rsrc(this->b_ptr(s));
+            const int ka = this->a_klim(s), kb = this->b_klim(s);
+            unsigned char *base = this->smem + slot * C::SLOT;
+            unsigned voff[UNITS];
+            if (!refill) {
 #pragma unroll
-            for (int i = 0; i < C::OA::U; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t *)(base + C::OA::lds_off(i, this->wave)), W,
-                                                          this->oa.voff_in(i), 0, 0, 0);
+                for (int u = 0; u < UNITS; ++u)
+                    voff[u] = 0;
+            } else if (likely_full<W>(this->full(ka, kb))) {
 #pragma unroll
-            for (int i = 0; i < C::OB::U; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rb, (lds_t *)(base + C::LA::BYTES + C::OB::lds_off(i, this->wave)), W, this->ob.voff_in(i), 0, 0,
-                    0);
-            return;
+                for (int i = 0; i < C::OA::U; ++i)
+                    voff[i] = this->oa.voff_in(i);
+#pragma unroll
+                for (int i = 0; i < C::OB::U; ++i)
+                    voff[C::OA::U + i] = this->ob.voff_in(i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::OA::U; ++i)
+                    voff[i] = this->oa.voff(i, this->a_rows, ka);
+#pragma unroll
+                for (int i = 0; i < C::OB::U; ++i)
+                    voff[C::OA::U + i] = this->ob.voff(i, kb, this->b_cols);
+            }
+            constexpr int J = Tile::TAIL_OPS;
+            this->tile.tail_with([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if (refill)
+                    static_for<j * UNITS / J, (j + 1) * UNITS / J>([&](auto uc) {
+                        constexpr int u = decltype(uc)::value;
+                        if constexpr (u < C::OA::U)
+                            lds_dma<W>(ra, base + C::OA::lds_off(u, this->wave), voff[u]);
+                        else
+                            lds_dma<W>(rb, base + C::LA::BYTES + C::OB::lds_off(u - C::OA::U, this->wave), voff[u]);
+                    });
+            });
         }
-#pragma unroll
-        for (int i = 0; i < C::OA::U; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_t *)(base + C::OA::lds_off(i, this->wave)), W,
-                                                      this->oa.voff(i, this->a_rows, ka), 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < C::OB::U; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_t *)(base + C::LA::BYTES + C::OB::lds_off(i, this->wave)), W,
-                this->ob.voff(i, kb, this->b_cols), 0, 0, 0);
     }
     // each slice is OA::U + OB::U fill instructions of this wave
     template <int P>
@@ -840,7 +972,9 @@ __global__ void __launch_bounds__(64 * Cfg::Tile::WAVES) sgemm_kernel(GemmArgs g
     ops.oa.init(ops.lane, ops.wave, g.lda);
     ops.ob.init(ops.lane, ops.wave, g.ldb);
     ops.tile.init(tid);
-    if constexpr (PIPED)
+    if constexpr (PIPED && SplitTile<Tile>::value && W == 16)
+        piped_schedule_split<S>(T, ops);
+    else if constexpr (PIPED)
         piped_schedule<S>(T, ops);
     else
         sync_schedule<S>(T, ops);

@@ -298,7 +298,7 @@ int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
                : ((M + 255) / 256) * ((N + 127) / 128) >= 512           ? MGEMM_TILE_256x128
                                                                           : MGEMM_TILE_128x128;
     const int bm = tile == MGEMM_TILE_128x128 ? 128 : 256, bn = tile == MGEMM_TILE_256x256 ? 256 : 128;
-    const int waves = tile == MGEMM_TILE_256x256 ? 8 : kWaves;
+    const int waves = tile == MGEMM_TILE_256x256 ? MGEMM_H256_WAVES : kWaves;
     constexpr int kps = kK16;
     mgemm_plan_t p;
     std::memset(&p, 0, sizeof p);
@@ -379,6 +379,14 @@ struct Recorder {
     void wait() { put(2, P, 0); }
     void barrier() { put(3, 0, 0); }
     void compute(int s, int slot) { put(4, s, slot); }
+    void head(int s, int slot) { put(7, s, slot); }
+    void body(int s, int slot) { put(4, s, slot); }
+    void tail(int s) { put(8, s, 0); }
+    void tail_issue(int tprev, int s, int slot, bool refill) {
+        if (refill)
+            issue(s, slot);
+        tail(tprev);
+    }
     template <int SET>
     void store(int slot) { put(5, SET, slot); }
     template <int SET>
@@ -667,13 +675,22 @@ int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K, const float *A, int64_t
 }
 
 int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *events, int cap) {
-    if (stages < 1 || slices < 0 || cap < 0 || (cap > 0 && events == nullptr) || (kind != 0 && kind != 1) ||
+    if (stages < 1 || slices < 0 || cap < 0 || (cap > 0 && events == nullptr) || kind < 0 || kind > 2 ||
         (fill_mode != MGEMM_FILL_SYNC && fill_mode != MGEMM_FILL_PIPED) ||
-        (kind == 1 && fill_mode != MGEMM_FILL_PIPED) ||
+        (kind != 0 && fill_mode != MGEMM_FILL_PIPED) ||
         stages > (fill_mode == MGEMM_FILL_PIPED ? kMaxPipedStages : kMaxSyncStages))
         return MGEMM_ERR_ARG;
     Recorder r{events, cap, 0};
-    if (fill_mode == MGEMM_FILL_PIPED) {
+    if (kind == 2) {
+        switch (stages) {
+        case 1: piped_schedule_split<1>(slices, r); break;
+        case 2: piped_schedule_split<2>(slices, r); break;
+        case 3: piped_schedule_split<3>(slices, r); break;
+        case 4: piped_schedule_split<4>(slices, r); break;
+        case 5: piped_schedule_split<5>(slices, r); break;
+        default: piped_schedule_split<6>(slices, r); break;
+        }
+    } else if (fill_mode == MGEMM_FILL_PIPED) {
         switch (stages) {
         case 1: piped_schedule<1>(slices, r); break;
         case 2: piped_schedule<2>(slices, r); break;

@@ -81,6 +81,70 @@ MG_HD inline void piped_schedule(int T, Ops &ops) {
     }
 }
 
+// Asynchronous ring with each compute split in three: head(slice, slot)
+// issues the LDS reads of the slice's first k step, body(slice, slot)
+// runs every k step but the last, whose reads it completes, and tail(slice)
+// runs the last k step from registers alone. Slice t-1's tail is placed
+// after slice t's head, so its matrix instructions cover the latency of
+// those reads instead of every wave waiting on them after the barrier, and
+// the refill of the slot just released is spread over those instructions
+// (tail_issue): issued as one burst, every wave's fills queue at the CU's
+// address unit and each wave stalls, in order, with the matrix pipe idle.
+// Each accumulator still sees the k steps in the same order, so results equal
+// piped_schedule's. The barrier of iteration t follows body(t-1), after
+// which the wave reads nothing more from slice t-1's slot: releasing it
+// there is safe although tail(t-1) has not run yet.
+template <int S, class Ops>
+MG_HD inline void piped_schedule_split(int T, Ops &ops) {
+    static_assert(S >= 1 && S <= kMaxPipedStages, "stages must be 1 .. 6");
+    if constexpr (S == 1) {
+        for (int t = 0; t < T; ++t) {
+            ops.issue(t, 0);
+            ops.template wait<0>();
+            ops.barrier();
+            ops.head(t, 0);
+            if (t > 0)
+                ops.tail(t - 1);
+            ops.body(t, 0);
+            ops.barrier();
+        }
+    } else {
+        // iteration 0 is peeled (it has no tail), so in the loop the tail
+        // is on the straight path: a tail in two branches, one of them with
+        // the refill spread over it, would give the accumulators two register
+        // assignments to reconcile
+        for (int s = 0; s < S - 1 && s < T; ++s)
+            ops.issue(s, s);
+        const auto wait_for = [&](int t) {
+            // slices issued after slice t so far: t+1 .. min(t+S-2, T-1)
+            const int pending = (t + S - 2 < T ? t + S - 2 : T - 1) - t;
+            static_for<0, S - 1>([&](auto p) {
+                if (pending == p.value)
+                    ops.template wait<p.value>();
+            });
+        };
+        if (T > 0) {
+            wait_for(0);
+            ops.barrier();
+            ops.head(0, 0);
+            if (S - 1 < T)
+                ops.issue(S - 1, S - 1);
+            ops.body(0, 0);
+        }
+        for (int t = 1; t < T; ++t) {
+            wait_for(t);
+            ops.barrier();
+            ops.head(t, t % S);
+            // tail(t-1), with the refill of the slot just released spread
+            // over its matrix instructions (none in the last S-1 iterations)
+            ops.tail_issue(t - 1, t + S - 1, (t + S - 1) % S, t + S - 1 < T);
+            ops.body(t, t % S);
+        }
+    }
+    if (T > 0)
+        ops.tail(T - 1);
+}
+
 // Synchronous ring: global -> registers -> LDS. Ops provides:
 //   load<SET>(slice)      issue global->register loads of `slice` into set SET
 //   store<SET>(slot)      write register set SET to LDS `slot` (waits on loads)

@@ -234,12 +234,17 @@ int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K,
 
 /*
  * Record the stage schedule that a kernel's ring executes for `slices` K
- * slices (fill_mode, stages as above; kind 0 = GEMM, 1 = tile copy), as
+ * slices (fill_mode, stages as above; kind 0 = fp32 GEMM, 1 = tile copy,
+ * 2 = the 16-bit GEMM's asynchronous ring, whose computes are split so that
+ * one slice's last k step overlaps the next slice's first LDS reads), as
  * produced by the very template the kernels instantiate. Each event is 3 ints
  * {op, a, b} written to events[0 .. 3*cap): op 1 = issue(slice a -> slot b),
  * 2 = wait(at most a slices of this wave in flight), 3 = barrier,
- * 4 = compute(slice a from slot b), 5 = store register set a -> slot b
- * (sync fill), 6 = load slice a into register set b (sync fill).
+ * 4 = compute(slice a from slot b; for kind 2 every k step but the last),
+ * 5 = store register set a -> slot b (sync fill), 6 = load slice a into
+ * register set b (sync fill), 7 = head(issue the first k step's LDS reads of
+ * slice a from slot b; kind 2), 8 = tail(the last k step of slice a, from
+ * registers; kind 2). Kinds 1 and 2 exist for MGEMM_FILL_PIPED only.
  * Returns the number of events (which may exceed cap; only cap are written),
  * or MGEMM_ERR_ARG (also for MGEMM_FILL_PIPED_WS, whose waves follow
  * separate filling and computing loops). Host only; no device needed.

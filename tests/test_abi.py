@@ -141,13 +141,17 @@ def test_lds_per_stage_matches_the_pages_budget():
 
 # ---- the ring schedule the kernels execute ---------------------------------
 
-def simulate_piped(events, S, T):
+def simulate_piped(events, S, T, split=False):
     """Check an asynchronous-ring trace: every slice issued once in order; a
     slot is refilled only after a barrier that follows the compute on its
     previous slice; compute(t) follows a wait that leaves slice t complete and
-    a barrier after it; in flight never exceeds S-1 during compute (S for S=1)."""
+    a barrier after it; in flight never exceeds S-1 during compute (S for S=1).
+    With split computes, head(t) (the first LDS reads) obeys the same rules as
+    compute(t) and comes right before it, apart from tail(t-1); tail(t) (no
+    LDS access) follows compute(t), in order, and every slice gets one."""
     issued, done = [], set()
     slot_of = {}
+    tails, headed = [], None
     slot_busy = {}  # slot -> slice computed-from but not yet released by a barrier
     last_compute_released = True
     computed = []
@@ -174,17 +178,28 @@ def simulate_piped(events, S, T):
             for s in list(done):
                 barrier_after_wait.add(s)
             slot_busy.clear()
-        elif op == 4:  # compute a from slot b
+        elif op in (4, 7):  # compute (or head) of slice a from slot b
+            assert split == (op == 7 or headed is not None), "head and compute must pair up"
             assert a == len(computed), "compute out of order"
-            assert a in barrier_after_wait, f"slice {a} computed before wait+barrier"
+            assert a in barrier_after_wait, f"slice {a} read before wait+barrier"
             assert slot_of[a] == b
             inflight = [s for s in issued if s not in done]
             assert len(inflight) <= max(S - 1, 0)
-            computed.append(a)
+            if op == 7:
+                assert headed is None
+                headed = a
+            else:
+                assert not split or headed == a, f"compute of slice {a} without its head"
+                headed = None
+                computed.append(a)
             slot_busy[b] = a
+        elif op == 8 and split:  # tail of slice a: registers only
+            assert a == len(tails) and a in computed, f"tail of slice {a} out of order"
+            tails.append(a)
         else:
             raise AssertionError(f"unexpected op {op}")
     assert issued == list(range(T)) and computed == list(range(T))
+    assert not split or tails == list(range(T))
 
 
 def simulate_sync(events, S, T):
@@ -244,11 +259,41 @@ def test_ring_schedule(S, fill):
         assert m.mgemm_ring_trace(1, S, 1, 5) == m.mgemm_ring_trace(0, S, 1, 5)
 
 
+@pytest.mark.parametrize("S", range(1, 7))
+def test_split_ring_schedule(S):
+    """The 16-bit GEMM's ring: the piped schedule with each compute split into
+    head / body / tail, the previous slice's tail after the next one's head."""
+    for T in list(range(0, 14)) + [31, 97]:
+        ev = m.mgemm_ring_trace(2, S, 1, T)
+        simulate_piped(ev, S, T, split=True)
+        # removing heads and tails leaves exactly the unsplit ring
+        assert [e for e in ev if e[0] not in (7, 8)] == m.mgemm_ring_trace(0, S, 1, T)
+        # the overlap itself: tail(t-1) sits between head(t) and compute(t),
+        # and so does the refill issued after the barrier (S >= 2), which
+        # tail_issue spreads over the tail's matrix instructions
+        for t in range(1, T):
+            k = ev.index((7, t, t % S if S > 1 else 0))
+            refill = S > 1 and t + S - 1 < T
+            between = ev[k + 1:k + 2 + refill]
+            assert (8, t - 1, 0) in between and ev[k + 2 + refill][0] == 4
+            assert not refill or between[0] == (1, t + S - 1, (t + S - 1) % S)
+    # a tail before its compute, or a missing head, is caught
+    ev = m.mgemm_ring_trace(2, S, 1, 4)
+    bad = list(ev)
+    t0 = bad.pop(bad.index((8, 0, 0)))
+    bad.insert(bad.index((4, 0, 0)), t0)
+    with pytest.raises(AssertionError):
+        simulate_piped(bad, S, 4, split=True)
+    with pytest.raises(AssertionError):
+        simulate_piped([e for e in ev if e[:2] != (7, 2)], S, 4, split=True)
+
+
 def test_ring_trace_rejects_bad_arguments():
     assert m.lib().mgemm_ring_trace(0, 7, 1, 3, None, 0) == m.ERR_ARG
     assert m.lib().mgemm_ring_trace(0, 4, 0, 3, None, 0) == m.ERR_ARG
     assert m.lib().mgemm_ring_trace(1, 2, 0, 3, None, 0) == m.ERR_ARG
-    assert m.lib().mgemm_ring_trace(2, 2, 1, 3, None, 0) == m.ERR_ARG
+    assert m.lib().mgemm_ring_trace(3, 2, 1, 3, None, 0) == m.ERR_ARG
+    assert m.lib().mgemm_ring_trace(2, 2, 0, 3, None, 0) == m.ERR_ARG
 
 
 def test_simulators_catch_planted_schedule_bugs():
