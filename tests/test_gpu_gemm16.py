@@ -89,6 +89,31 @@ def test_every_variant(fmt, layout):
                     assert same_bits(C, ref), (fmt, layout, tile, fill, S)
 
 
+@pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192])
+def test_few_slices(K):
+    """1, 2 and 3 K slices with 16-byte loads: the split ring's first
+    iteration (no tail yet), its last ones (a tail but no refill) and the tail
+    after the loop, on every tile, fill and depth. Exact on the 2^-4 grid
+    and bit-identical across variants."""
+    fmt, M, N = "bf16", 300, 264
+    A = datagen.matrix16(5, M, K, fmt, kind="coarse")
+    B = datagen.matrix16(6, K, N, fmt, kind="coarse")
+    want = oracle.gemm16_f64(A, B, fmt).astype(np.float32)
+    Ad, Bd = dev16(A, fmt), dev16(B, fmt)
+    assert m.plan16(M, N, K, a_ptr=Ad.data_ptr(), b_ptr=Bd.data_ptr())["load_bytes"] == 16
+    for tile in TILES16:
+        for fill in ("sync", "piped"):
+            for S in (1, 2, 3, 4):
+                if not fits(tile, S) or (fill == "sync" and S == 4):
+                    continue
+                Cd = out_device(M, N, N + 3)
+                m.gemm16(Ad, Bd, Cd, stages=S, fill=fill, tile=tile)
+                torch.cuda.synchronize()
+                full = full_rows(Cd)
+                assert np.all(full[:, N:] == SENTINEL), (K, tile, fill, S)
+                assert same_bits(full[:, :N], want), (K, tile, fill, S)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_coarse_grid_exact(fmt):
     M, N, K = 384, 256, 1024
