@@ -25,6 +25,7 @@ namespace mgemm {
 
 constexpr int kAttnBK = 64;                 // keys per ring slice
 constexpr int kAttnWaves = 8;               // waves per block (2 per SIMD), 32 queries each
+constexpr float kLazyRescale = 8.0f;        // log2 headroom before the running maximum moves
 constexpr int kAttnBQ = 32 * kAttnWaves;    // queries per block
 constexpr int kAttnThreads = 64 * kAttnWaves;
 
@@ -195,10 +196,11 @@ struct AttnTile {
     // Online softmax over one slice's scores s (replaced by the
     // probabilities). x = c s with c = scale log2(e) >= 0 (init() folds a
     // negative scale into the sign of Q); p = 2^(x - m) is formed as one fma,
-    // 2^(fma(s, c, -m)), with m the running maximum of x, c times the raw
-    // maximum. Keys >= seq_k (FULL false: the last slice) get p = 0. O is
-    // rescaled unless every lane's maximum stayed put (alpha == 1 exactly:
-    // x * 1 == x, so skipping changes no bit).
+    // 2^(fma(s, c, -m)), with m a running reference at most kLazyRescale
+    // below the maximum of x so far (c times the raw maximum). Keys >= seq_k
+    // (FULL false: the last slice) get p = 0. O is rescaled unless every
+    // lane's reference stayed put (alpha == 1 exactly: x * 1 == x, so
+    // skipping changes no bit).
     template <bool FULL>
     __device__ void softmax(f32x16 (&s)[NKT], int key0, int seq_k) {
         const int h = lane >> 5;
@@ -209,7 +211,14 @@ struct AttnTile {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 ext = fmaxf(ext, FULL || valid(kt, i) ? s[kt][i] : -__builtin_inff());
-        const float mnew = fmaxf(mrow, c * pair_max(ext)); // finite: key0 < seq_k
+        // the running maximum moves only when the slice's exceeds it by more
+        // than kLazyRescale (log2 units); otherwise the probabilities of this
+        // slice may reach 2^kLazyRescale, which fp32 sums and the 16-bit P
+        // hold with the same relative rounding. Softmax does not depend on
+        // the shift, so O = sum p v / sum p is unchanged, and most slices
+        // then skip the rescale of O below.
+        const float mcand = fmaxf(mrow, c * pair_max(ext)); // finite: key0 < seq_k
+        const float mnew = mcand > mrow + kLazyRescale ? mcand : mrow;
         const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
         float rs = 0.0f;
 #pragma unroll

@@ -139,6 +139,27 @@ def test_scales(scale):
     check(O, Q, K, V, fmt, scale, f"scale {scale}")
 
 
+@pytest.mark.parametrize("scale", [1.0, 4.0, 6.0])
+def test_scores_rising_across_slices(scale):
+    """Scores that climb with the key index, by about 1.4, 5.8 and 8.7 (log2
+    units) per 64-key slice: the running reference stays behind the true
+    maximum for several slices (probabilities up to 2^8) or moves every
+    slice, and the result still matches the oracle."""
+    fmt, B, H, Sq, Sk, D = "bf16", 1, 1, 64, 1000, 64
+    q = np.zeros((Sq, D), np.float32)
+    q[:, 0] = 1.0
+    q[:, 1] = np.linspace(-0.5, 0.5, Sq)
+    k = np.zeros((Sk, D), np.float32)
+    k[:, 0] = np.arange(Sk) / 64.0
+    k[:, 1] = np.cos(np.arange(Sk))
+    Q, K = (torch.from_numpy(x).to(torch.bfloat16).cuda().view(B, H, -1, D) for x in (q, k))  # rounded to bf16
+    V = dev_qkv(31, B, H, Sk, D, fmt)
+    O = m.attention(Q, K, V, scale=scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O).all())
+    check(O, Q, K, V, fmt, scale, f"rising scores, scale {scale}")
+
+
 def test_one_key_returns_its_value_row():
     fmt, D = "bf16", 128
     Q, K, V = dev_qkv(10, 1, 1, 70, D, fmt), dev_qkv(11, 1, 1, 1, D, fmt), dev_qkv(12, 1, 1, 1, D, fmt)
