@@ -141,6 +141,22 @@ def profile_mode(args):
           f"{m.plan_attention(B_, H_, S_, S_, 128)}", flush=True)
 
 
+def peak_clock_mhz():
+    """The device's peak shader clock in MHz from the HIP runtime
+    (hipDeviceGetAttribute with hipDeviceAttributeClockRate, which is entry 5
+    of hipDeviceAttribute_t and reports kHz), or None if unavailable. The
+    clock under load is lower and varies: the kernel timings are the truth."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    v = ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) != 0:
+        return None
+    return round(v.value / 1000.0, 1)
+
+
 def timed_launches(fn, warmup=3, runs=10, repeats=1):
     """The pages' protocol ("pipelined_gemm.cu", timeKernel): warm-up launches,
     then the mean of `runs` launches between two events; `repeats` blocks give
@@ -223,8 +239,11 @@ def main():
     achieved_tflops = flop / (kernel_ms * 1e-3) / 1e12
 
     props = torch.cuda.get_device_properties(0)
+    arch = getattr(props, "gcnArchName", "")
     extra = {
-        "device": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+        "device": props.name or f"AMD {arch.split(':')[0]} ({props.multi_processor_count} CUs)", "arch": arch,
+        "cus": props.multi_processor_count, "peak_clock_mhz": peak_clock_mhz(),
+        "l2_bytes": getattr(props, "L2_cache_size", None),
         "pct_fp32_peak_8192": round(100.0 * value / 1e3 / PEAK_FP32_TFLOPS, 2),
         "kernel_ms": round(kernel_ms, 4), "parity_gate": "piped == sync (bitwise, full output)",
         "plan": plan,
