@@ -636,9 +636,10 @@ int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, f
     a.ldd = (int)ldd;
     a.tcols = (int)((cols + 63) / 64);
     const int64_t ntiles = ((rows + 63) / 64) * a.tcols;
-    if (ntiles >= kMaxExtent)
+    if (ntiles > kMaxExtent - 4) // tile ids of a final partial run stay below 2^31
         return MGEMM_ERR_UNSUPPORTED;
     a.ntiles = (int)ntiles;
+    a.run_log2 = a.tcols >= 4 ? 2 : 0;
     const void *fn = copy_kernel(stages, W, vst);
     // persistent grid: as many blocks as fit on the device at once
     static std::atomic<int> occ_cache[kMaxPipedStages][2][2];

@@ -310,7 +310,7 @@ def test_copy_page_example_pattern():
 
 @pytest.mark.parametrize("case", [
     (1000, 777, 781, 790, 0, 0), (64, 64, 64, 64, 0, 0), (130, 200, 200, 204, 1, 0), (5, 3, 3, 3, 0, 1),
-    (257, 1024, 1024, 1024, 0, 0)])
+    (257, 1024, 1024, 1024, 0, 0), (130, 300, 300, 303, 0, 2), (65, 1000, 1001, 1000, 3, 0)])
 def test_copy_ragged(case):
     rows, cols, lds, ldd, os_, od = case
     x = datagen.matrix("normal", datagen.SEED_COPY, rows, cols)
