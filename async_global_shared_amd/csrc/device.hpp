@@ -381,27 +381,14 @@ struct Mfma16Tile {
                     acc[a][b][i] = __builtin_nanf("");
     }
 
-    // The four transposing reads of one k step (2 column tiles x 2 row
-    // quads) and the wait for them, in one asm block: the compiler's wait
-    // pass does not model ds_read_b64_tr_b16 against in-flight LDS-DMA fills
-    // and would drain the whole prefetch (vmcnt(0)) before it, although the
-    // ring's own wait and barrier already made this slot's slice visible.
-    // The outputs are early-clobber: a read lands while later reads of the
-    // block still need their address registers.
-    template <int OFF0, int OFF1>
-    __device__ static void read_b(unsigned a0, unsigned a1, i16x4 &b00, i16x4 &b01, i16x4 &b10, i16x4 &b11) {
-        asm volatile("ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
-                     "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
-                     "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
-                     "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
-                     "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(b00), "=&v"(b01), "=&v"(b10), "=&v"(b11)
-                     : "v"(a0), "v"(a1), "i"(OFF0), "i"(OFF1));
-    }
-
-#ifndef MGEMM_H16_PIPE
-#define MGEMM_H16_PIPE 1
-#endif
+    // The LDS reads are issued from inline asm, and a separate asm wait
+    // lists their destinations as outputs: the compiler's wait pass does not
+    // model ds_read_b64_tr_b16 against in-flight LDS-DMA fills and would
+    // drain the whole prefetch (vmcnt(0)) before it, although the ring's own
+    // wait and barrier already made this slot's slice visible. Outputs are
+    // early-clobber where one asm block issues several reads: a read may land
+    // while later reads of the block still need their address registers.
+    //
     // One k step's operands: WTM A rows (16 bytes each) and two transposing
     // B reads per column tile.
     struct Frag {
@@ -472,11 +459,7 @@ struct Mfma16Tile {
         });
     }
 
-#if MGEMM_H16_PIPE
-#ifndef MGEMM_H16_SPLIT
-#define MGEMM_H16_SPLIT 1
-#endif
-    static constexpr bool kSplit = MGEMM_H16_SPLIT;
+    static constexpr bool kSplit = true;
     __device__ void lane_addrs(const unsigned char *As, const unsigned char *Bs, unsigned &as, unsigned *ab) const {
         const int h = lane >> 5, q = lane & 15, g16 = (lane >> 4) & 1;
         as = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)As;
@@ -549,50 +532,6 @@ struct Mfma16Tile {
         body(As, Bs);
         tail();
     }
-#else
-    __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
-        static_assert(WTN == 2, "read_b covers two 32-column tiles");
-        const int h = lane >> 5, l32 = lane & 31, q = lane & 15, g16 = (lane >> 4) & 1;
-        // lane part of the B read address: row 8h + q/4 of each 16-row k step,
-        // columns n .. n+3 with n = 32(WTN wn + tb) + 16 g16 + 4(q%4); the k
-        // step and the row quad add 16 ks + 4 r2 rows (immediate offsets: the
-        // swizzle depends on the row mod 4 only)
-        unsigned ab[WTN];
-        const unsigned bs = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)Bs;
-#pragma unroll
-        for (int tb = 0; tb < WTN; ++tb) {
-            const int k = 8 * h + (q >> 2);
-            const int n = 32 * WTN * wn + 32 * tb + 16 * g16 + 4 * (q & 3);
-            ab[tb] = bs + LB::pos(k, n >> 3) * 16 + (n & 7) * 2;
-        }
-        static_for<0, KPS / 16>([&](auto ksc) {
-            constexpr int ks = decltype(ksc)::value;
-            u32x4 a[WTM];
-#pragma unroll
-            for (int ta = 0; ta < WTM; ++ta) {
-                const int m = 32 * WTM * wm + 32 * ta + l32;
-                a[ta] = *(const u32x4 *)(As + LA::pos(m, 2 * ks + h) * 16);
-            }
-            i16x4 b[WTN][2];
-            read_b<(16 * ks) * LB::CPR * 16, (16 * ks + 4) * LB::CPR * 16>(ab[0], ab[1], b[0][0], b[0][1], b[1][0],
-                                                                            b[1][1]);
-#pragma unroll
-            for (int ta = 0; ta < WTM; ++ta)
-#pragma unroll
-                for (int tb = 0; tb < WTN; ++tb) {
-                    const i16x4 lo = b[tb][0], hi = b[tb][1];
-                    typedef short i16x8 __attribute__((ext_vector_type(8)));
-                    const i16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    if constexpr (BF16)
-                        acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, a[ta]), __builtin_bit_cast(bf16x8, bv), acc[ta][tb], 0, 0, 0);
-                    else
-                        acc[ta][tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(f16x8, a[ta]), __builtin_bit_cast(f16x8, bv), acc[ta][tb], 0, 0, 0);
-                }
-        });
-    }
-#endif
 
     __device__ void store(float *C, int ldc, int m0, int n0, int M, int N, bool) const {
         const int h = lane >> 5, l32 = lane & 31;
@@ -656,12 +595,8 @@ struct CfgH256x128 {
     static constexpr int BM = 256, BN = 128;
 };
 template <bool BF16>
-#ifndef MGEMM_H256_WAVES
-#define MGEMM_H256_WAVES 8
-#endif
 struct CfgH256x256 { // 8 waves (2 per SIMD), each 128 x 64 as in the 256 x 128 tile
-    using Tile = typename std::conditional<MGEMM_H256_WAVES == 8, Mfma16Tile<4, 2, 2, 4, BF16>,
-                                           Mfma16Tile<4, 4, 2, 2, BF16>>::type;
+    using Tile = Mfma16Tile<4, 2, 2, 4, BF16>;
     static constexpr int BM = 256, BN = 256;
 };
 

@@ -298,7 +298,7 @@ int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
                : ((M + 255) / 256) * ((N + 127) / 128) >= 512           ? MGEMM_TILE_256x128
                                                                           : MGEMM_TILE_128x128;
     const int bm = tile == MGEMM_TILE_128x128 ? 128 : 256, bn = tile == MGEMM_TILE_256x256 ? 256 : 128;
-    const int waves = tile == MGEMM_TILE_256x256 ? MGEMM_H256_WAVES : kWaves;
+    const int waves = tile == MGEMM_TILE_256x256 ? 8 : kWaves;
     constexpr int kps = kK16;
     mgemm_plan_t p;
     std::memset(&p, 0, sizeof p);
