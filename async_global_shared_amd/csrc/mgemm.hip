@@ -315,7 +315,10 @@ int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
     p.fill_mode = fill;
     const int slice_bytes = (bm * kps + kps * bn) * 2;
     p.lds_bytes = stages * slice_bytes;
-    p.loads_per_slice = slice_bytes / (64 * W) / waves;
+    // per filling wave: with 16-byte loads the 8-wave tile's asynchronous
+    // ring fills from 4 waves only
+    const int fill_waves = (waves == 8 && fill == MGEMM_FILL_PIPED && W == 16) ? 4 : waves;
+    p.loads_per_slice = slice_bytes / (64 * W) / fill_waves;
     p.max_vmcnt = fill == MGEMM_FILL_PIPED ? std::min(63, std::max(0, stages - 2) * p.loads_per_slice) : 0;
     if (p.lds_bytes > kLdsBytes)
         return MGEMM_ERR_UNSUPPORTED;

@@ -206,7 +206,8 @@ typedef struct mgemm_plan {
     int stages;
     int fill_mode;
     int lds_bytes;     /* LDS per block: stages * (bm*bk + bk*bn) * 4 */
-    int loads_per_slice; /* vector-memory instructions per wave per K slice */
+    int loads_per_slice; /* vector-memory instructions per filling wave per K slice (the 16-bit
+                            256x256 tile fills its asynchronous ring from 4 of its 8 waves) */
     int max_vmcnt;     /* largest s_waitcnt vmcnt immediate the schedule uses */
 } mgemm_plan_t;
 

@@ -534,7 +534,9 @@ def test_gemm16_plans():
     assert (p["bm"], p["bn"], p["threads"], p["blocks"]) == (256, 256, 512, 32 * 32)
     assert m.plan16(4096, 4096, 4096)["bn"] == 256 and m.plan16(4096, 2048, 64)["bn"] == 128
     assert m.plan16(2048, 2048, 2048)["bm"] == 128
-    assert p["lds_bytes"] == 2 * (256 + 256) * bk * 2 and p["loads_per_slice"] == (256 + 256) * bk * 2 // 1024 // 8
+    # the asynchronous ring of the 8-wave tile fills from 4 waves; the register-staged one from all 8
+    assert p["lds_bytes"] == 2 * (256 + 256) * bk * 2 and p["loads_per_slice"] == (256 + 256) * bk * 2 // 1024 // 4
+    assert m.plan16(8192, 8192, 8192, fill="sync")["loads_per_slice"] == (256 + 256) * bk * 2 // 1024 // 8
     # rings beyond the 160 KiB of LDS are refused
     st, _ = m.mgemm_plan_gemm16(8192, 8192, 8192, A0, 8192, B0, 8192, C0, 8192, 1, 3, 1, 4)
     assert st == (m.ERR_UNSUPPORTED if 3 * (256 + 256) * bk * 2 > 160 * 1024 else m.OK)
