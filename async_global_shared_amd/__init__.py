@@ -64,6 +64,7 @@ def lib():
         L.mgemm_plan_sgemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci,
                                        ctypes.POINTER(Plan)]
         L.mgemm_ring_trace.argtypes = [ci, ci, ci, ci, ctypes.POINTER(ctypes.c_int), ci]
+        L.mgemm_fill_trace.argtypes = [ci, ci, ci, ctypes.POINTER(ctypes.c_int), ci]
         L.mgemm_gemm16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, vp]
         L.mgemm_plan_gemm16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci,
                                         ctypes.POINTER(Plan)]
@@ -76,7 +77,7 @@ def lib():
         L.mgemm_status_string.argtypes = [ci]
         L.mgemm_status_string.restype = ctypes.c_char_p
         for f in (L.mgemm_sgemm, L.mgemm_sgemm_ex, L.mgemm_tile_copy, L.mgemm_plan_sgemm,
-                  L.mgemm_ring_trace, L.mgemm_version, L.mgemm_blocks_per_cu, L.mgemm_gemm16,
+                  L.mgemm_ring_trace, L.mgemm_fill_trace, L.mgemm_version, L.mgemm_blocks_per_cu, L.mgemm_gemm16,
                   L.mgemm_plan_gemm16, L.mgemm_attention, L.mgemm_plan_attention):
             f.restype = ci
         _lib = L
@@ -144,6 +145,20 @@ def mgemm_blocks_per_cu(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, comp
     st = lib().mgemm_blocks_per_cu(M, N, K, A, lda, B, ldb, C, ldc, stages, fill_mode, compute, tile, loader,
                                    ctypes.byref(out))
     return st, out.value
+
+
+def mgemm_fill_trace(kind: int, load_bytes: int, fill_mode: int):
+    """One slice's loader map as (header, events): header = (slot bytes, rows0,
+    cols0, rows1, cols1); events = (operand, wave, lds byte, row, col, layout
+    byte) per lane and unit (see include/mgemm.h)."""
+    n = lib().mgemm_fill_trace(kind, load_bytes, fill_mode, None, 0)
+    if n < 0:
+        raise MgemmError(n, "mgemm_fill_trace")
+    buf = (ctypes.c_int * (6 * max(n, 1)))()
+    lib().mgemm_fill_trace(kind, load_bytes, fill_mode, buf, n)
+    ev = [tuple(buf[6 * i:6 * i + 6]) for i in range(n)]
+    assert ev[0][0] == -1
+    return ev[0][1:], ev[1:]
 
 
 def mgemm_ring_trace(kind: int, stages: int, fill_mode: int, slices: int):

@@ -99,7 +99,7 @@ struct Operand {
     int off[U];
     int lane, wave;
 
-    __device__ void rc(int i, int &r, int &c) const {
+    MG_HD void rc(int i, int &r, int &c) const {
         const int g = i * WAVES + wave;
         if constexpr (W == 16) {
             const int p = g * 64 + lane;
@@ -111,7 +111,7 @@ struct Operand {
             c = 4 * L::col4(q >> 2) + (q & 3);
         }
     }
-    __device__ void init(int lane_, int wave_, int ld) {
+    MG_HD void init(int lane_, int wave_, int ld) {
         lane = lane_;
         wave = wave_;
 #pragma unroll
@@ -122,7 +122,7 @@ struct Operand {
         }
     }
     // byte offset within the operand's region of a slot, for unit i of wave w
-    __device__ static constexpr int lds_off(int i, int wave) { return (i * WAVES + wave) * 64 * W; }
+    MG_HD static constexpr int lds_off(int i, int wave) { return (i * WAVES + wave) * 64 * W; }
 
     __device__ unsigned voff(int i, int rowlim, int collim) const {
         int r, c;
@@ -761,8 +761,9 @@ constexpr int kPipedFillWaves = W == 16 ? FillWaves<Tile>::value : Tile::WAVES;
 template <class Tile, int W>
 struct PipedOps : GemmCtx<Tile, W, kPipedFillWaves<Tile, W>> {
     using C = GemmCtx<Tile, W, kPipedFillWaves<Tile, W>>;
-    // this wave issues fills (block-uniform per wave: a scalar test)
-    __device__ bool fills() const { return C::FW == Tile::WAVES || this->wave < C::FW; }
+    // wave w issues fills (block-uniform per wave: a scalar test)
+    MG_HD static constexpr bool fills_wave(int w) { return C::FW == Tile::WAVES || w < C::FW; }
+    __device__ bool fills() const { return fills_wave(this->wave); }
     static constexpr int UNITS = C::OA::U + C::OB::U;
     // Slice s's fill instructions one unit at a time (units 0 .. OA::U-1 are
     // A's, the rest B's; FULL: the slice lies inside A and B). The buffer

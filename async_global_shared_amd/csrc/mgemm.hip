@@ -505,6 +505,92 @@ const void *select_attention(const mgemm_plan_t &p, int dtype) {
 
 } // namespace
 
+// ---- host-side fill map for mgemm_fill_trace ------------------------------------------
+// One slice's fill instructions, enumerated with the operand types and fill
+// wave rules the kernels instantiate.
+
+struct FillRecorder {
+    int *ev;
+    int cap, n;
+    void put(int a, int b, int c, int d, int e, int f) {
+        if (n < cap) {
+            int *p = ev + 6 * n;
+            p[0] = a, p[1] = b, p[2] = c, p[3] = d, p[4] = e, p[5] = f;
+        }
+        ++n;
+    }
+};
+
+// operand `which` of a slot: its loader type O (units split among the waves
+// that fill it), its layout L, byte offset `base` in the slot; wave w fills
+// when `fills(w)`
+template <class O, class L, int W, class F>
+void trace_operand(FillRecorder &rec, int which, int base, int waves, int fw, F fills) {
+    for (int w = 0; w < waves; ++w) {
+        if (!fills(w))
+            continue;
+        for (int lane = 0; lane < 64; ++lane) {
+            O o;
+            o.init(lane, w % fw, 0);
+            for (int u = 0; u < O::U; ++u) {
+                int r, c;
+                o.rc(u, r, c);
+                rec.put(which, w, base + O::lds_off(u, w) + lane * W, r, c, base + L::pos(r, c >> 2) * 16 + (c & 3) * 4);
+            }
+        }
+    }
+}
+
+template <class Cfg, int W, bool PIPED>
+void trace_gemm_fill(FillRecorder &rec) {
+    using Tile = typename Cfg::Tile;
+    using C = typename std::conditional<PIPED, typename PipedOps<Tile, W>::C, typename SyncOps<Tile, W, 1>::C>::type;
+    auto fills = [](int w) { return !PIPED || PipedOps<Tile, W>::fills_wave(w); };
+    rec.put(-1, C::SLOT, C::LA::kRows, C::LA::kCols, C::LB::kRows, C::LB::kCols);
+    trace_operand<typename C::OA, typename C::LA, W>(rec, 0, 0, Tile::WAVES, C::FW, fills);
+    trace_operand<typename C::OB, typename C::LB, W>(rec, 1, C::LA::BYTES, Tile::WAVES, C::FW, fills);
+}
+
+template <int D, int W>
+void trace_attention_fill(FillRecorder &rec) {
+    using Tile = AttnTile<D, true>;
+    using C = AttnCtx<Tile, W>;
+    auto all = [](int) { return true; };
+    rec.put(-1, C::SLOT, C::LK::kRows, C::LK::kCols, C::LV::kRows, C::LV::kCols);
+    trace_operand<typename C::OK, typename C::LK, W>(rec, 0, 0, Tile::WAVES, Tile::WAVES, all);
+    trace_operand<typename C::OV, typename C::LV, W>(rec, 1, C::LK::BYTES, Tile::WAVES, Tile::WAVES, all);
+}
+
+template <int W>
+void trace_copy_fill(FillRecorder &rec) {
+    using Ops = CopyOps<W, true>;
+    auto producer = [](int w) { return w < Ops::PW; };
+    rec.put(-1, Ops::SLOT, CopyLayout::kRows, CopyLayout::kCols, 0, 0);
+    trace_operand<typename Ops::OP, CopyLayout, W>(rec, 0, 0, kCopyWaves, Ops::PW, producer);
+}
+
+template <int W, bool PIPED>
+bool fill_trace_kind(int kind, FillRecorder &rec) {
+    switch (kind) {
+    case 0: trace_gemm_fill<CfgValu64, W, PIPED>(rec); return true;
+    case 1: trace_gemm_fill<CfgValu128, W, PIPED>(rec); return true;
+    case 2: trace_gemm_fill<CfgMfma64, W, PIPED>(rec); return true;
+    case 3: trace_gemm_fill<CfgMfma128, W, PIPED>(rec); return true;
+    case 4: trace_gemm_fill<CfgMfma256x128, W, PIPED>(rec); return true;
+    case 5: trace_gemm_fill<CfgH128<true>, W, PIPED>(rec); return true;
+    case 6: trace_gemm_fill<CfgH256x128<true>, W, PIPED>(rec); return true;
+    case 7: trace_gemm_fill<CfgH256x256<true>, W, PIPED>(rec); return true;
+    case 8: trace_attention_fill<64, W>(rec); return true;
+    case 9: trace_attention_fill<128, W>(rec); return true;
+    case 10:
+        if (!PIPED)
+            return false;
+        trace_copy_fill<W>(rec);
+        return true;
+    default: return false;
+    }
+}
+
 extern "C" {
 
 const char *mgemm_status_string(int s) {
@@ -676,6 +762,17 @@ int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K, const float *A, int64_t
         return MGEMM_ERR_LAUNCH;
     *blocks_per_cu = occ;
     return MGEMM_OK;
+}
+
+int mgemm_fill_trace(int kind, int load_bytes, int fill_mode, int *events, int cap) {
+    if ((load_bytes != 16 && load_bytes != 4) || (fill_mode != MGEMM_FILL_SYNC && fill_mode != MGEMM_FILL_PIPED) ||
+        cap < 0 || (cap > 0 && events == nullptr))
+        return MGEMM_ERR_ARG;
+    FillRecorder rec{events, cap, 0};
+    const bool piped = fill_mode == MGEMM_FILL_PIPED;
+    const bool ok = load_bytes == 16 ? (piped ? fill_trace_kind<16, true>(kind, rec) : fill_trace_kind<16, false>(kind, rec))
+                                     : (piped ? fill_trace_kind<4, true>(kind, rec) : fill_trace_kind<4, false>(kind, rec));
+    return ok ? rec.n : MGEMM_ERR_ARG;
 }
 
 int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *events, int cap) {

@@ -252,6 +252,27 @@ int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K,
  */
 int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *events, int cap);
 
+/*
+ * Record where one K slice's fill instructions put each element: the
+ * loader map of a kernel's ring, enumerated with the operand types and the
+ * filling-wave rules the kernels instantiate (the tile loader and zero-fill
+ * row of the method: coalesced 16-byte or 4-byte lanes, each lane's
+ * destination in the LDS slot). kind: 0 fp32 VALU 64x64, 1 VALU 128x128,
+ * 2 fp32 MFMA 64x64, 3 MFMA 128x128, 4 MFMA 256x128, 5 16-bit 128x128,
+ * 6 16-bit 256x128, 7 16-bit 256x256, 8 attention head dim 64, 9 head dim
+ * 128, 10 tile copy (MGEMM_FILL_PIPED only); load_bytes 16 or 4;
+ * fill_mode MGEMM_FILL_SYNC (register-staged) or MGEMM_FILL_PIPED.
+ * Events are 6 ints written to events[0 .. 6*cap). The first is a header
+ * {-1, slot bytes, rows and 32-bit columns of operand 0, rows and columns of
+ * operand 1}. Each other event is one lane's load of one unit:
+ * {operand (0: A / K / the copy tile, 1: B / V), wave, LDS byte offset of
+ * the written data in the slot, row, first 32-bit column, LDS byte offset
+ * at which the compute side's layout reads that element}. Returns the
+ * number of events (may exceed cap; only cap are written) or MGEMM_ERR_ARG.
+ * Host only; no device needed.
+ */
+int mgemm_fill_trace(int kind, int load_bytes, int fill_mode, int *events, int cap);
+
 #ifdef __cplusplus
 }
 #endif

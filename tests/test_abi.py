@@ -1,9 +1,10 @@
 """Host-side tests of libmgemm: exports, argument validation, launch plans,
-the ring schedule the kernels execute, and evidence in the generated gfx950
-ISA. No GPU is touched: every call here returns before any HIP call."""
+the ring schedule and the loader map the kernels execute, and evidence in
+the generated gfx950 ISA. No GPU is touched: every call here returns before any HIP call."""
 import os
 import re
 
+import numpy as np
 import pytest
 
 import async_global_shared_amd as m
@@ -18,7 +19,7 @@ def test_exports_every_declared_symbol():
     src = open(HEADER).read()
     names = set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(mgemm_[a-z_]+)\s*\(", src, re.M))
     assert {"mgemm_sgemm", "mgemm_sgemm_ex", "mgemm_tile_copy", "mgemm_status_string", "mgemm_version",
-            "mgemm_plan_sgemm", "mgemm_ring_trace"} <= names
+            "mgemm_plan_sgemm", "mgemm_ring_trace", "mgemm_fill_trace"} <= names
     L = m.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -286,6 +287,57 @@ def test_split_ring_schedule(S):
         simulate_piped(bad, S, 4, split=True)
     with pytest.raises(AssertionError):
         simulate_piped([e for e in ev if e[:2] != (7, 2)], S, 4, split=True)
+
+
+FILL_KINDS = {0: "fp32 VALU 64", 1: "fp32 VALU 128", 2: "fp32 MFMA 64", 3: "fp32 MFMA 128", 4: "fp32 MFMA 256x128",
+              5: "16-bit 128", 6: "16-bit 256x128", 7: "16-bit 256x256", 8: "attention D64", 9: "attention D128",
+              10: "tile copy"}
+
+
+@pytest.mark.parametrize("kind", sorted(FILL_KINDS))
+@pytest.mark.parametrize("W", [16, 4])
+@pytest.mark.parametrize("fill", [0, 1])
+def test_fill_map_covers_the_slot_once(kind, W, fill):
+    """One slice's loader map, from the kernels' own operand types and
+    filling-wave rules: every byte of the LDS slot is written exactly once,
+    every element of each operand's slice is fetched exactly once, and each
+    lands where the compute side's layout reads it."""
+    if kind == 10 and fill == 0:
+        assert m.lib().mgemm_fill_trace(kind, W, fill, None, 0) == m.ERR_ARG
+        return
+    (slot, r0, c0, r1, c1), ev = m.mgemm_fill_trace(kind, W, fill)
+    written = np.zeros(slot, np.int32)
+    fetched = [np.zeros((r0, c0), np.int32), np.zeros((r1, c1), np.int32)]
+    words = W // 4
+    for op, wave, lds, r, c, want in ev:
+        assert 0 <= lds and lds + W <= slot, (FILL_KINDS[kind], op, wave, lds)
+        written[lds:lds + W] += 1
+        assert lds == want, (FILL_KINDS[kind], op, wave, r, c, lds, want)
+        fetched[op][r, c:c + words] += 1
+    assert np.all(written == 1), (FILL_KINDS[kind], int((written != 1).sum()))
+    for op in (0, 1):
+        assert np.all(fetched[op] == 1), (FILL_KINDS[kind], op)
+    waves = {w for _, w, *_ in ev}
+    if kind == 7 and fill == 1 and W == 16:
+        assert waves == {0, 1, 2, 3}  # the 8-wave tile's asynchronous ring fills from one wave per SIMD
+    elif kind == 10:
+        assert waves == {0, 1, 2, 3}  # the copy's filling waves
+    else:
+        assert waves == set(range(8 if kind in (7, 8, 9) else 4))
+
+
+def test_fill_map_catches_a_misplaced_unit():
+    """The checker above rejects a loader that writes one unit of one wave
+    at its neighbour's place."""
+    (slot, *_), ev = m.mgemm_fill_trace(7, 16, 1)
+    bad = [(op, w, lds + 1024 if (w, op) == (1, 0) and i % 97 == 0 else lds, r, c, want)
+           for i, (op, w, lds, r, c, want) in enumerate(ev)]
+    written = np.zeros(slot + 2048, np.int32)
+    ok = True
+    for op, w, lds, r, c, want in bad:
+        written[lds:lds + 16] += 1
+        ok &= lds == want
+    assert not ok and np.any(written[:slot] != 1)
 
 
 def test_ring_trace_rejects_bad_arguments():
