@@ -291,12 +291,32 @@ int plan_gemm16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
         return MGEMM_ERR_ALIAS;
     const bool b128_ok = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 && N % 8 == 0;
     const int W = b128_ok ? 16 : 4;
-    if (tile == MGEMM_TILE_AUTO)
-        // the largest tile that still gives every CU a block (measured at 4096^3 and 8192^3);
-        // with 4-byte loads the 8-wave tile would spill (every wave holds 256 VGPRs at most)
-        tile = (W == 16 && ((M + 255) / 256) * ((N + 255) / 256) >= 256) ? MGEMM_TILE_256x256
-               : ((M + 255) / 256) * ((N + 127) / 128) >= 512           ? MGEMM_TILE_256x128
-                                                                          : MGEMM_TILE_128x128;
+    if (tile == MGEMM_TILE_AUTO) {
+        // The tile with the least estimated time: each of the 256 CUs works
+        // through ceil(blocks / 256) tiles, each costing its area over the
+        // tile's relative throughput (bf16 8192^3, piped S=2: 256x256 1.0,
+        // 256x128 0.92, 128x128 0.80). Fewer, larger tiles win while they
+        // still fill the CUs' rounds; with 4-byte loads the 8-wave tile would
+        // spill (every wave holds 256 VGPRs at most), so it is not a candidate.
+        struct Cand {
+            int tile, bm, bn;
+            double eff;
+        };
+        const Cand cands[] = {{MGEMM_TILE_256x256, 256, 256, 1.0},
+                              {MGEMM_TILE_256x128, 256, 128, 0.92},
+                              {MGEMM_TILE_128x128, 128, 128, 0.80}};
+        double best = 0.0;
+        for (const Cand &c : cands) {
+            if (c.tile == MGEMM_TILE_256x256 && W != 16)
+                continue;
+            const int64_t blocks = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+            const double t = (double)((blocks + 255) / 256) * c.bm * c.bn / c.eff;
+            if (tile == MGEMM_TILE_AUTO || t < best) {
+                tile = c.tile;
+                best = t;
+            }
+        }
+    }
     const int bm = tile == MGEMM_TILE_128x128 ? 128 : 256, bn = tile == MGEMM_TILE_256x256 ? 256 : 128;
     const int waves = tile == MGEMM_TILE_256x256 ? 8 : kWaves;
     constexpr int kps = kK16;

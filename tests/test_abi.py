@@ -586,6 +586,9 @@ def test_gemm16_plans():
     assert (p["bm"], p["bn"], p["threads"], p["blocks"]) == (256, 256, 512, 32 * 32)
     assert m.plan16(4096, 4096, 4096)["bn"] == 256 and m.plan16(4096, 2048, 64)["bn"] == 128
     assert m.plan16(2048, 2048, 2048)["bm"] == 128
+    # 240 blocks of 256x256 (one round of the 256 CUs) beat 960 of 128x128 (four rounds)
+    assert (m.plan16(3000, 5000, 4000)["bm"], m.plan16(3000, 5000, 4000)["bn"]) == (256, 256)
+    assert m.plan16(3000, 5000, 4000, lda=4002, ldb=5002)["bn"] == 128  # 4-byte loads: never the 8-wave tile
     # the asynchronous ring of the 8-wave tile fills from 4 waves; the register-staged one from all 8
     assert p["lds_bytes"] == 2 * (256 + 256) * bk * 2 and p["loads_per_slice"] == (256 + 256) * bk * 2 // 1024 // 4
     assert m.plan16(8192, 8192, 8192, fill="sync")["loads_per_slice"] == (256 + 256) * bk * 2 // 1024 // 8
