@@ -848,7 +848,8 @@ struct PipedOps : GemmCtx<Tile, W, kPipedFillWaves<Tile, W>> {
             });
         }
     }
-    // each slice is OA::U + OB::U fill instructions of this wave
+    // each slice is OA::U + OB::U fill instructions of a filling wave (a
+    // wave that fills nothing has none in flight: its waits pass at once)
     template <int P>
     __device__ void wait() {
         wait_vm<P *(C::OA::U + C::OB::U)>();
