@@ -164,6 +164,17 @@ struct ValuTile {
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = __builtin_nanf("");
     }
+    // An empty asm that reads and writes every accumulator: the slice's FMAs
+    // are then issued before whatever follows in program order, instead of
+    // being sunk below the next slice's (branchy) LDS stores, which would
+    // keep all of the slice's LDS fragments live across them.
+    __device__ void pin() {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; j += 4)
+                asm volatile("" : "+v"(acc[i][j]), "+v"(acc[i][j + 1]), "+v"(acc[i][j + 2]), "+v"(acc[i][j + 3]));
+    }
     __device__ int row(int h, int i) const { return 64 * h + 4 * tr + i; }
     __device__ int col(int h) const { return 64 * h + 4 * tc; }
 
@@ -247,6 +258,7 @@ struct MfmaTile {
                     acc[a][b][i] = 0.0f;
     }
 
+    __device__ void pin() {} // MFMA results stay where the MFMAs are issued
     __device__ void poison() {
 #pragma unroll
         for (int a = 0; a < WTM; ++a)
@@ -371,6 +383,7 @@ struct Mfma16Tile {
                 for (int i = 0; i < 16; ++i)
                     acc[a][b][i] = 0.0f;
     }
+    __device__ void pin() {} // MFMA results stay where the MFMAs are issued
     __device__ void poison() {
 #pragma unroll
         for (int a = 0; a < WTM; ++a)
@@ -890,6 +903,10 @@ struct SyncOps : GemmCtx<Tile, W> {
 #pragma unroll
         for (int i = 0; i < C::OB::U; ++i)
             vb[SET][i] = ld(rb, this->ob.voff(i, kb, this->b_cols));
+    }
+    __device__ void compute(int t, int slot) {
+        C::compute(t, slot);
+        this->tile.pin();
     }
     template <int SET>
     __device__ void store(int slot) {

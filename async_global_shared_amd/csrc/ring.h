@@ -153,8 +153,11 @@ MG_HD inline void piped_schedule_split(int T, Ops &ops) {
 // For S >= 2 (a double buffer built from synchronous loads, as in the
 // "async copy pipeline" article's benchmark), S-1 register sets keep S-1
 // slices in flight: iteration t issues slice t+S-1, computes slice t, then
-// stores slice t+1 into its slot and barriers. Register-set indices are
-// compile-time constants (the loop is unrolled by S-1).
+// stores slice t+1 into its slot and barriers. The register set is picked by
+// a uniform branch around the loads and stores only: one compute per loop
+// iteration, so the compute tile's accumulators have one home (two unrolled
+// copies of the compute, each under its own branch, made the compiler keep
+// a second copy of them).
 template <int S, class Ops>
 MG_HD inline void sync_schedule(int T, Ops &ops) {
     static_assert(S >= 1 && S <= kMaxSyncStages, "stages must be 1, 2 or 3");
@@ -176,18 +179,22 @@ MG_HD inline void sync_schedule(int T, Ops &ops) {
             ops.template store<0>(0);
             ops.barrier();
         }
-        for (int t0 = 0; t0 < T; t0 += R) {
-            static_for<0, R>([&](auto u) {
-                const int t = t0 + u.value;
-                if (t < T) {
-                    if (t + R < T)
-                        ops.template load<u.value>(t + R);
-                    ops.compute(t, t % S);
-                    if (t + 1 < T)
-                        ops.template store<(u.value + 1) % R>((t + 1) % S);
-                    ops.barrier();
-                }
-            });
+        for (int t = 0; t < T; ++t) {
+            const int u = t % R;
+            if (t + R < T)
+                static_for<0, R>([&](auto v) {
+                    if (u == v.value)
+                        ops.template load<v.value>(t + R);
+                });
+            ops.compute(t, t % S);
+            if (t + 1 < T) {
+                const int w = (t + 1) % R;
+                static_for<0, R>([&](auto v) {
+                    if (w == v.value)
+                        ops.template store<v.value>((t + 1) % S);
+                });
+            }
+            ops.barrier();
         }
     }
 }
