@@ -422,12 +422,17 @@ struct AttnSyncOps : AttnCtx<Tile, W> {
         else
             return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
     }
+    // A slice past the last one (rows <= 0) masks every lane; its descriptors
+    // are built on slice 0's addresses so that none points past K or V.
     template <int SET>
     __device__ void load(int s) {
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(this->k_ptr(s));
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(this->v_ptr(s));
         const int rows = this->rows(s);
-        if (__builtin_expect(rows >= kAttnBK, 1)) {
+        const int sp = rows > 0 ? s : 0;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(this->k_ptr(sp));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(this->v_ptr(sp));
+        // two register sets or more: one load form, kept ahead of the compute
+        // (as in the GEMM's register-staged ring)
+        if (NSET == 1 && __builtin_expect(rows >= kAttnBK, 1)) {
 #pragma unroll
             for (int i = 0; i < C::OK::U; ++i)
                 vk[SET][i] = ld(rk, this->ok.voff_in(i));
@@ -442,6 +447,8 @@ struct AttnSyncOps : AttnCtx<Tile, W> {
 #pragma unroll
         for (int i = 0; i < C::OV::U; ++i)
             vv[SET][i] = ld(rv, this->ov.voff(i, rows, C::COLS));
+        if constexpr (NSET > 1)
+            __builtin_amdgcn_sched_barrier(0);
     }
     template <int SET>
     __device__ void store(int slot) {

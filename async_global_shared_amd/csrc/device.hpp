@@ -883,12 +883,19 @@ struct SyncOps : GemmCtx<Tile, W> {
         else
             return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
     }
+    // A slice past the last one (kb <= 0) masks every lane; its descriptors
+    // are built on slice 0's addresses so that none points past the operands.
+    // With two register sets or more the loads take one form only (masked
+    // offsets) and stay ahead of the compute: alternative load blocks made
+    // the compiler's wait counts drain the newest slice before each store,
+    // and loads in the compute's block were sunk below it.
     template <int SET>
     __device__ void load(int s) {
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(s));
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(s));
         const int ka = this->a_klim(s), kb = this->b_klim(s);
-        if (likely_full<W>(this->full(ka, kb))) {
+        const int sp = kb > 0 ? s : 0;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(sp));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(sp));
+        if (NSET == 1 && likely_full<W>(this->full(ka, kb))) {
 #pragma unroll
             for (int i = 0; i < C::OA::U; ++i)
                 va[SET][i] = ld(ra, this->oa.voff_in(i));
@@ -903,6 +910,8 @@ struct SyncOps : GemmCtx<Tile, W> {
 #pragma unroll
         for (int i = 0; i < C::OB::U; ++i)
             vb[SET][i] = ld(rb, this->ob.voff(i, kb, this->b_cols));
+        if constexpr (NSET > 1)
+            __builtin_amdgcn_sched_barrier(0);
     }
     __device__ void compute(int t, int slot) {
         C::compute(t, slot);

@@ -146,18 +146,26 @@ MG_HD inline void piped_schedule_split(int T, Ops &ops) {
 }
 
 // Synchronous ring: global -> registers -> LDS. Ops provides:
-//   load<SET>(slice)      issue global->register loads of `slice` into set SET
+//   load<SET>(slice)      issue global->register loads of `slice` into set SET;
+//                         a slice >= T must issue the same loads with every
+//                         lane masked (zeros, no memory access)
 //   store<SET>(slot)      write register set SET to LDS `slot` (waits on loads)
 //   barrier(), compute(slice, slot) as above
 // S == 1 is the pages' matmulTileSync: load, store, barrier, compute, barrier.
 // For S >= 2 (a double buffer built from synchronous loads, as in the
 // "async copy pipeline" article's benchmark), S-1 register sets keep S-1
 // slices in flight: iteration t issues slice t+S-1, computes slice t, then
-// stores slice t+1 into its slot and barriers. The register set is picked by
-// a uniform branch around the loads and stores only: one compute per loop
-// iteration, so the compute tile's accumulators have one home (two unrolled
-// copies of the compute, each under its own branch, made the compiler keep
-// a second copy of them).
+// stores slice t+1 into its slot and barriers.
+// With two sets or more the loop runs whole groups of S-1 iterations,
+// stopping before the last slice, so that register-set indices are
+// compile-time constants and every load, compute and store in its body is
+// unconditional (a load past the last
+// slice is the masked one, and its set is never stored). Conditional loads
+// or stores there made the compiler's wait counts assume the worst path and
+// drain the slice issued last before each store; a set index chosen at run
+// time made it copy the sets between branches; computes under a branch each
+// made it keep a second copy of the accumulators. The last 1 .. S-1 slices
+// run after the loop.
 template <int S, class Ops>
 MG_HD inline void sync_schedule(int T, Ops &ops) {
     static_assert(S >= 1 && S <= kMaxSyncStages, "stages must be 1, 2 or 3");
@@ -179,23 +187,37 @@ MG_HD inline void sync_schedule(int T, Ops &ops) {
             ops.template store<0>(0);
             ops.barrier();
         }
-        for (int t = 0; t < T; ++t) {
-            const int u = t % R;
-            if (t + R < T)
-                static_for<0, R>([&](auto v) {
-                    if (u == v.value)
-                        ops.template load<v.value>(t + R);
-                });
-            ops.compute(t, t % S);
-            if (t + 1 < T) {
-                const int w = (t + 1) % R;
-                static_for<0, R>([&](auto v) {
-                    if (w == v.value)
-                        ops.template store<v.value>((t + 1) % S);
-                });
+        if constexpr (R == 1) {
+            // one register set: its store waits for the newest loads, so
+            // conditional loads cost no wait precision
+            for (int t = 0; t < T; ++t) {
+                if (t + 1 < T)
+                    ops.template load<0>(t + 1);
+                ops.compute(t, t % S);
+                if (t + 1 < T)
+                    ops.template store<0>((t + 1) % S);
+                ops.barrier();
             }
-            ops.barrier();
+            return;
         }
+        const int Tm = T > 0 ? (T - 1) / R * R : 0;
+        for (int t0 = 0; t0 < Tm; t0 += R)
+            static_for<0, R>([&](auto u) {
+                const int t = t0 + u.value;
+                ops.template load<u.value>(t + R);
+                ops.compute(t, t % S);
+                ops.template store<(u.value + 1) % R>((t + 1) % S);
+                ops.barrier();
+            });
+        static_for<0, R>([&](auto u) {
+            const int t = Tm + u.value;
+            if (t < T) {
+                ops.compute(t, t % S);
+                if (t + 1 < T)
+                    ops.template store<(u.value + 1) % R>((t + 1) % S);
+                ops.barrier();
+            }
+        });
     }
 }
 

@@ -243,7 +243,8 @@ int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K,
  * 2 = wait(at most a slices of this wave in flight), 3 = barrier,
  * 4 = compute(slice a from slot b; for kind 2 every k step but the last),
  * 5 = store register set a -> slot b (sync fill), 6 = load slice a into
- * register set b (sync fill), 7 = head(issue the first k step's LDS reads of
+ * register set b (sync fill; a >= slices is a load with every lane masked,
+ * whose set is never stored), 7 = head(issue the first k step's LDS reads of
  * slice a from slot b; kind 2), 8 = tail(the last k step of slice a, from
  * registers; kind 2). Kinds 1 and 2 exist for MGEMM_FILL_PIPED only.
  * Returns the number of events (which may exceed cap; only cap are written),

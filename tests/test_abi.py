@@ -207,22 +207,31 @@ def simulate_sync(events, S, T):
     """Check a synchronous-ring trace: each slice loaded once, in order, into a
     register set that is free; stored from the set holding it into the slot it
     is computed from; a barrier separates store and compute; a slot is
-    overwritten only after a barrier that follows the compute on it."""
+    overwritten only after a barrier that follows the compute on it. A load
+    of a slice past the last (the masked load that keeps the loop body free
+    of branches) comes after every real one and its set is never stored."""
     R = max(S - 1, 1)
     sets = {}
     loaded = []
+    masked = []
     slot_holds = {}
     visible = set()
     slot_busy = {}
     computed = []
     for op, a, b in events:
-        if op == 6:  # load slice a into set b
-            assert a == len(loaded) and 0 <= b < R
+        if op == 6 and a >= T:  # masked load into set b
+            assert len(loaded) == T and 0 <= b < R, "masked load before the last real one"
             assert sets.get(b) is None, f"register set {b} reused before its store"
+            sets[b] = "masked"
+            masked.append(a)
+        elif op == 6:  # load slice a into set b
+            assert a == len(loaded) and 0 <= b < R
+            assert sets.get(b) is None or sets[b] == "masked", f"register set {b} reused before its store"
             sets[b] = a
             loaded.append(a)
         elif op == 5:  # store set a -> slot b
             assert sets.get(a) is not None, "store of an empty register set"
+            assert sets[a] != "masked", "store of a masked load"
             assert slot_busy.get(b) is None, f"slot {b} overwritten before a barrier released it"
             assert slot_holds.get(b) is None or slot_holds[b] in computed, f"slot {b} overwritten before use"
             s = sets.pop(a)
@@ -241,6 +250,8 @@ def simulate_sync(events, S, T):
         else:
             raise AssertionError(op)
     assert loaded == list(range(T)) and computed == list(range(T))
+    assert len(masked) <= R - 1 if S > 1 else not masked
+    return masked
 
 
 @pytest.mark.parametrize("S,fill", [(S, 1) for S in range(1, 7)] + [(S, 0) for S in (1, 2, 3)])
@@ -255,7 +266,9 @@ def test_ring_schedule(S, fill):
             if S >= 2:
                 assert waits == [min(T - 1, t + S - 2) - t for t in range(T)]
         else:
-            simulate_sync(ev, S, T)
+            masked = simulate_sync(ev, S, T)
+            # two register sets: the grouped loop's one masked load when T is odd
+            assert masked == ([T] if S == 3 and T >= 3 and T % 2 else [])
     if fill == 1:
         assert m.mgemm_ring_trace(1, S, 1, 5) == m.mgemm_ring_trace(0, S, 1, 5)
 
