@@ -673,6 +673,55 @@ def test_isa_gemm16(isa, cfg, bf16):
                 assert "v_pk_fma_f32" not in body and "v_pk_add_f32" not in body and "v_pk_mul_f32" not in body
 
 
+def _store_waits(lines):
+    """The vmcnt each ds_write waits for: groups of consecutive ds_writes,
+    each write carrying the last s_waitcnt vmcnt(N) of its group (None if
+    the group has had none)."""
+    out, cur, last = [], None, None
+    for raw in lines:
+        x = raw.strip()
+        if not x or x.startswith(";"):
+            continue
+        mm = re.match(r"s_waitcnt .*vmcnt\((\d+)\)", x)
+        if mm:
+            last = int(mm.group(1))
+            continue
+        if x.startswith("ds_write"):
+            cur = [] if cur is None else cur
+            cur.append(last)
+        elif cur is not None and not x.startswith("s_waitcnt"):
+            out.append(cur)
+            cur, last = None, None
+        if x.startswith(("buffer_load", "s_barrier")):
+            last = None
+    if cur:
+        out.append(cur)
+    return out
+
+
+SYNC3 = ([(c, lambda c=c: _name(c, 3, False, 16)) for c in CFGS]
+         + [(c, lambda c=c: _name16(c, True, 3, False, 16)) for c in ("CfgH128", "CfgH256x128")]
+         + [(f"attention D{D}", lambda D=D: _attn_name(D, True, 3, False, 16)) for D in (64, 128)])
+
+
+@pytest.mark.parametrize("what,name", SYNC3, ids=[w for w, _ in SYNC3])
+def test_isa_sync_ring_keeps_the_newer_slice_in_flight(isa, what, name):
+    """The two-register-set synchronous ring stores slice t+1 while slice
+    t+2's loads are still in flight: its two steps' ds_writes wait with
+    vmcnt >= L, the loads of one set (the prologue's store of slice 0 has L
+    writes). Branches in the loop body used to make these waits drain to
+    vmcnt(0..L-1)."""
+    groups = _store_waits(isa[name()])
+    L = len(groups[0])
+    overlapped = 0
+    for g in groups[1:]:
+        w = None
+        for x in g:
+            w = x if x is not None else w
+            overlapped += w is not None and w >= L
+    assert overlapped >= 2 * L, (what, L, groups)
+
+
 def _regs(operand):
     """VGPR indices named by one operand ('v7', 'v[30:33]'), else empty."""
     mm = re.fullmatch(r"v(\d+)", operand) or re.fullmatch(r"v\[(\d+):(\d+)\]", operand)
