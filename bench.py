@@ -181,7 +181,7 @@ def timed_launches(fn, warmup=3, runs=10, repeats=1):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the GEMM would shard by row bands of C, one band per GPU, with B broadcast)", file=sys.stderr)
         sys.exit(2)
     if args.profile:

@@ -340,7 +340,7 @@ def test_fill_map_covers_the_slot_once(kind, W, fill):
 
 
 def test_fill_map_catches_a_misplaced_unit():
-    """The checker above rejects a loader that writes one unit of one wave
+    """The fill-map test above rejects a loader that writes one unit of one wave
     at its neighbour's place."""
     (slot, *_), ev = m.mgemm_fill_trace(7, 16, 1)
     bad = [(op, w, lds + 1024 if (w, op) == (1, 0) and i % 97 == 0 else lds, r, c, want)
@@ -362,7 +362,7 @@ def test_ring_trace_rejects_bad_arguments():
 
 
 def test_simulators_catch_planted_schedule_bugs():
-    """The checkers above reject the classic ring mistakes."""
+    """The ring simulators above reject the classic ring mistakes."""
     good = m.mgemm_ring_trace(0, 3, 1, 6)
     # compute before waiting: drop the first wait
     bad = list(good)
