@@ -78,6 +78,8 @@ SHAPES = [  # B, H, Sq, Sk, D
     (1, 3, 200, 300, 64),
     (1, 1, 33, 1, 128),
     (1, 1, 1, 513, 128),
+    (1, 2, 70, 192, 128),  # 3 key slices: the two-set synchronous ring's masked last load
+    (1, 1, 90, 256, 64),  # 4 key slices: no masked load
 ]
 
 

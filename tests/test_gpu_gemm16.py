@@ -89,12 +89,13 @@ def test_every_variant(fmt, layout):
                     assert same_bits(C, ref), (fmt, layout, tile, fill, S)
 
 
-@pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192])
+@pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192, 256, 320])
 def test_few_slices(K):
-    """1, 2 and 3 K slices with 16-byte loads: the split ring's first
-    iteration (no tail yet), its last ones (a tail but no refill) and the tail
-    after the loop, on every tile, fill and depth. Exact on the 2^-4 grid
-    and bit-identical across variants."""
+    """1 to 5 K slices with 16-byte loads: the split ring's first iteration
+    (no tail yet), its last ones (a tail but no refill) and the tail after
+    the loop; the two-set synchronous ring's grouped loop with and without
+    its masked last load (odd and even slice counts). Every tile, fill and
+    depth; exact on the 2^-4 grid and bit-identical across variants."""
     fmt, M, N = "bf16", 300, 264
     A = datagen.matrix16(5, M, K, fmt, kind="coarse")
     B = datagen.matrix16(6, K, N, fmt, kind="coarse")

@@ -181,7 +181,7 @@ def test_coarse_grid_is_exact_for_every_variant(shape):
             assert same_bits(C, want), (shape, compute, tile, fill, S)
 
 
-@pytest.mark.parametrize("K", [1000, 1537, 16, 17])
+@pytest.mark.parametrize("K", [1000, 1537, 16, 17, 32, 47, 48, 64, 80, 96])
 def test_slice_sentinels(K):
     """A = 1, B[k, j] = floor(k/16) (and the mirror) give C = 16 T(T-1)/2 + rT
     exactly; a slice computed from the wrong ring slot changes the sum."""
