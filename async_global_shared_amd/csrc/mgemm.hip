@@ -24,7 +24,6 @@ namespace {
 
 constexpr int64_t kMaxLd = int64_t(1) << 21;     // 256 rows x 2^21 words x 4 B: in-block byte offsets stay below 2^31
 constexpr int64_t kMaxExtent = int64_t(1) << 31; // rows * ld per operand, in elements
-constexpr int64_t kAutoBigTileBlocks = 512;      // 128x128 tiles once they give >= 2 blocks per CU
 constexpr int kMaxStages16 = 4;                  // asynchronous ring depth of the 16-bit GEMM
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -92,8 +91,37 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
     }
 
     if (tile == MGEMM_TILE_AUTO) {
-        const int64_t nb128 = ((M + 127) / 128) * ((N + 127) / 128);
-        tile = nb128 >= kAutoBigTileBlocks ? MGEMM_TILE_128x128 : MGEMM_TILE_64x64;
+        // 64x64 or 128x128, whichever has the least estimated time: each of
+        // the 256 CUs works through ceil(blocks / 256) tiles, each costing
+        // its area over the tile's relative throughput (8192^3, piped S=2:
+        // 64x64 runs at 0.90 (VALU) / 0.91 (MFMA) of 128x128), slowed where
+        // few blocks share a CU: one wave issues a dependence-free FMA only
+        // every few cycles, so the VALU tile needs several waves per SIMD
+        // (measured 1.80x slower with one, 1.13x with two, 1.05x with three);
+        // the MFMA tile 1.1x with one. Resident blocks are capped by the
+        // ring's LDS and by the kernel's registers. Ties keep 128x128.
+        const bool valu = compute == MGEMM_COMPUTE_VALU;
+        struct Cand {
+            int tile, bm, bn, cap;
+            double eff;
+        };
+        const Cand cands[] = {{MGEMM_TILE_128x128, 128, 128, valu ? 4 : 5, 1.0},
+                              {MGEMM_TILE_64x64, 64, 64, 8, valu ? 0.90 : 0.91}};
+        double best = 0.0;
+        for (const Cand &c : cands) {
+            const int64_t blocks = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+            const int64_t per_cu = (blocks + 255) / 256;
+            const int slot = (c.bm + c.bn) * kBK * 4;
+            const int64_t lds_cap = std::max<int64_t>(1, kLdsBytes / (std::max(stages, 1) * slot));
+            const int64_t resident = std::min<int64_t>({per_cu, (int64_t)c.cap, lds_cap});
+            const double slow = valu ? (resident <= 1 ? 1.80 : resident == 2 ? 1.13 : resident == 3 ? 1.05 : 1.0)
+                                     : (resident <= 1 ? 1.10 : 1.0);
+            const double t = (double)per_cu * c.bm * c.bn / c.eff * slow;
+            if (tile == MGEMM_TILE_AUTO || t < best) {
+                tile = c.tile;
+                best = t;
+            }
+        }
     }
     const int bm = tile == MGEMM_TILE_256x128 ? 256 : tile == MGEMM_TILE_128x128 ? 128 : 64;
     const int bn = tile == MGEMM_TILE_64x64 ? 64 : 128;

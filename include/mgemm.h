@@ -58,7 +58,7 @@ struct mgemm_plan; /* defined below (mgemm_plan_t) */
 #define MGEMM_COMPUTE_MFMA 1 /* v_mfma_f32_32x32x2_f32 wave tiles */
 
 /* tile: block tile of C (BM x BN, K slice 16, 256 threads). */
-#define MGEMM_TILE_AUTO 0
+#define MGEMM_TILE_AUTO 0      /* 64x64 or 128x128, whichever a wave model of the CUs estimates faster */
 #define MGEMM_TILE_64x64 1   /* VALU: 4x4 micro-tile per thread (the pages' shape) */
 #define MGEMM_TILE_128x128 2 /* VALU: 8x8 micro-tile; MFMA: 2x2 32x32 tiles per wave */
 #define MGEMM_TILE_256x128 3 /* MFMA only: 4x2 32x32 tiles per wave (BM 256, BN 128) */

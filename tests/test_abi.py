@@ -99,7 +99,7 @@ def test_plan_tiles_loaders_and_lds():
     p = m.plan(4096, 4096, 4096, compute="mfma", stages=3)
     assert (p["bm"], p["blocks"], p["lds_bytes"], p["loads_per_slice"], p["max_vmcnt"]) == (128, 1024, 49152, 4, 4)
     # ragged, misaligned leading dimensions -> 4-byte loads
-    p = m.plan(4099, 3001, 1537, stages=3, lda=1537, ldb=3001, ldc=3001)
+    p = m.plan(4099, 3001, 1537, stages=3, tile="128x128", lda=1537, ldb=3001, ldc=3001)
     assert p["load_bytes"] == 4 and p["bm"] == 128 and p["blocks"] == 33 * 24 and p["slices"] == 97
     assert p["loads_per_slice"] == 16 and p["max_vmcnt"] == 16
     # tall-skinny keeps enough blocks with 64 x 64 tiles
@@ -116,6 +116,24 @@ def test_plan_tiles_loaders_and_lds():
     # deep rings fit the 160 KiB of LDS: 6 stages of 256x128x16 fp32 tiles
     p = m.plan(8192, 8192, 8192, stages=6, compute="mfma", tile="256x128")
     assert p["lds_bytes"] == 6 * (256 + 128) * 16 * 4 <= 160 * 1024
+
+
+# (M, N, K) -> automatic fp32 tile edge, for both compute tiles: the cases
+# measured on MI355X (ragged and tall-skinny, where 128x128 would leave CUs
+# with a partial last round or a lone block, and the large squares).
+AUTO_FP32 = {(4099, 3001, 1537): 64, (16384, 64, 4096): 64, (2048, 2048, 2048): 64, (256, 256, 256): 64,
+             (4096, 4096, 4096): 128, (8192, 8192, 8192): 128}
+
+
+@pytest.mark.parametrize("compute", ["valu", "mfma"])
+def test_auto_fp32_tile(compute):
+    for (M, N, K), edge in AUTO_FP32.items():
+        for S in (1, 2, 3):
+            p = m.plan(M, N, K, stages=S, compute=compute)
+            assert (p["bm"], p["bn"]) == (edge, edge), (compute, M, N, K, S)
+    # the ABI's plain entry point plans with the VALU tile and the same choice
+    st, pl = m.mgemm_plan_sgemm(4099, 3001, 1537, A0, 1537, B0, 3001, C0, 3001, 2, 1, 0, 0, 0)
+    assert st == m.OK and pl.bm == 64
 
 
 def test_plan_warp_specialised():
