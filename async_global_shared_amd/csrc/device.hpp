@@ -885,17 +885,20 @@ struct SyncOps : GemmCtx<Tile, W> {
     }
     // A slice past the last one (kb <= 0) masks every lane; its descriptors
     // are built on slice 0's addresses so that none points past the operands.
-    // With two register sets or more the loads take one form only (masked
-    // offsets) and stay ahead of the compute: alternative load blocks made
-    // the compiler's wait counts drain the newest slice before each store,
-    // and loads in the compute's block were sunk below it.
+    // With two register sets or more, 16-byte loads take one form only
+    // (masked offsets) and stay ahead of the compute: alternative load
+    // blocks made the compiler's wait counts drain the newest slice before
+    // each store, and loads in the compute's block were sunk below it.
+    // 4-byte loads keep the full-slice fast path: with four times the units,
+    // a selected offset per unit costs more registers than exact waits gain
+    // (VALU 128x128, S=3: 267 -> 182 VGPRs, 37 -> 63 TFLOP/s at 4099x3001x1537).
     template <int SET>
     __device__ void load(int s) {
         const int ka = this->a_klim(s), kb = this->b_klim(s);
         const int sp = kb > 0 ? s : 0;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(this->a_ptr(sp));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(this->b_ptr(sp));
-        if (NSET == 1 && likely_full<W>(this->full(ka, kb))) {
+        if ((NSET == 1 || W == 4) && likely_full<W>(this->full(ka, kb))) {
 #pragma unroll
             for (int i = 0; i < C::OA::U; ++i)
                 va[SET][i] = ld(ra, this->oa.voff_in(i));
