@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--compute", default="mfma", choices=["mfma", "valu"])
     p.add_argument("--no-extra", action="store_true", help="skip the tables after the timed region")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    p.add_argument("--oracle-full", action="store_true",
+                   help="also time the oracle once on the whole problem (all rows; about 20 s on 16 host cores)")
     p.add_argument("--profile", action="store_true",
                    help="only run a few launches of the timed GEMM, the 1 GiB tile copy (3 stages), a plain "
                         "1 GiB device copy (the calibration kernel for hardware byte counters), the 16-bit GEMM "
@@ -255,6 +257,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(Ad, Bd)
+        extra["oracle_timing"] = oracle_timing(Ad, Bd, datagen, full=args.oracle_full)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -472,6 +475,42 @@ def cpu_baseline(Ad, Bd, budget_s=12.0):
     return {"value": round(fl / dt / 1e9, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {Ad.shape[0]} rows of the {Ad.shape[0]}x{Bd.shape[1]}x{Ad.shape[1]} product "
                       f"(fp64 accumulate), {dt:.1f} s wall"}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_timing(Ad, Bd, datagen, full=False):
+    """The oracle on the host: the CPU model and thread count, one-thread
+    runs at 256^3 and 1024^3 on the seeded uniform inputs, and (with `full`)
+    one run over every row of the timed problem on all threads."""
+    import oracle
+    lib = oracle.load()
+    threads = oracle.num_threads(lib)
+    out = {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "threads": threads}
+    oracle.set_threads(1, lib)
+    try:
+        for n in (256, 1024):
+            A = datagen.matrix("uniform", datagen.SEED_A, n, n)
+            B = datagen.matrix("uniform", datagen.SEED_B, n, n)
+            dt, fl = oracle.timed_gemm_rows(A, B, n, lib=lib)
+            out[f"one_thread_{n}"] = {"s": round(dt, 3), "gflops": round(fl / dt / 1e9, 3)}
+    finally:
+        oracle.set_threads(threads, lib)
+    if full:
+        A_host, B_host = Ad.cpu().numpy(), Bd.cpu().numpy()
+        dt, fl = oracle.timed_gemm_rows(A_host, B_host, A_host.shape[0], lib=lib)
+        out[f"all_threads_full_{A_host.shape[0]}"] = {"s": round(dt, 2), "gflops": round(fl / dt / 1e9, 3)}
+    return out
 
 
 if __name__ == "__main__":

@@ -57,6 +57,8 @@ def _bind(lib):
     lib.oracle_copy_f32.argtypes = [i64, i64, fp, i64, fp, i64]
     lib.oracle_copy_f32.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
     lib.oracle_decode16.argtypes = [ctypes.c_uint16, ctypes.c_int]
     lib.oracle_decode16.restype = ctypes.c_double
     lib.oracle_gemm16_f64.argtypes = [i64, i64, i64, fp, i64, fp, i64, dp, i64, ctypes.c_int, ctypes.c_int]
@@ -144,6 +146,11 @@ def bound(K: int, Abs: np.ndarray, slack: float = 4.0) -> np.ndarray:
 
 def num_threads(lib=None) -> int:
     return int((lib or load()).oracle_num_threads())
+
+
+def set_threads(n: int, lib=None) -> None:
+    """Thread count of the oracle's parallel loops (timing only)."""
+    (lib or load()).oracle_set_threads(int(n))
 
 
 def timed_gemm_rows(A: np.ndarray, B: np.ndarray, rows: int, lib=None):

@@ -94,6 +94,18 @@ void oracle_copy_f32(int64_t rows, int64_t cols, const float *src, int64_t lds,
         memcpy(dst + r * ldd, src + r * lds, (size_t)cols * sizeof(float));
 }
 
+/* Thread count of the parallel loops (timing only: results do not depend on
+   it, each output element being one thread's sequential sum). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of threads the parallel loops above use. */
 int oracle_num_threads(void)
 {
