@@ -13,6 +13,9 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "attention.hpp"
 #include "device.hpp"
@@ -284,10 +287,54 @@ const void *select_gemm(const mgemm_plan_t &p) {
                                         : gemm_kernel<CfgMfma64>(p.stages, piped, p.load_bytes);
 }
 
-int launch(const void *fn, int blocks, void *arg, hipStream_t stream, int threads = kThreads) {
+int launch(const void *fn, int blocks, void *arg, hipStream_t stream, int threads = kThreads, int dyn_lds = 0) {
     void *args[] = {arg};
-    const hipError_t e = hipLaunchKernel(fn, dim3(blocks), dim3(threads), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(fn, dim3(blocks), dim3(threads), args, dyn_lds, stream);
     return e == hipSuccess ? MGEMM_OK : MGEMM_ERR_LAUNCH;
+}
+
+// Resident blocks per CU of a kernel with `dyn` bytes of dynamic LDS per
+// block, as the runtime computes them (cached; 0 if the query fails).
+int occupancy(const void *fn, int threads, int dyn) {
+    static std::mutex mu;
+    static std::map<std::pair<const void *, int>, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(fn, dyn);
+    const auto it = cache.find(key);
+    if (it != cache.end())
+        return it->second;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, threads, dyn) != hipSuccess)
+        occ = 0;
+    cache[key] = occ;
+    return occ;
+}
+
+// Residency cap of the fp32 GEMM. When each CU must take exactly one block
+// more than it holds (n = b + 1 blocks per CU with b = 3 or 4 resident), the
+// blocks of a round run in lockstep and the extra one then runs alone;
+// holding ceil(n/2) blocks instead splits the CU's tiles into two even
+// rounds. Measured (MFMA 128x128, N = K = 4096, TFLOP/s): piped S=3 with
+// 896 / 960 / 1024 tiles 111 / 110 / 116 -> 121 / 134 / 142; sync S=2 with
+// 1152 / 1280 tiles 107 / 117 -> 126 / 119; capping any other case (n = b,
+// n = b + 2) measured slower. The cap is imposed as unused dynamic LDS and
+// applied only if the runtime then reports exactly that residency. Returns
+// the dynamic LDS bytes per block (0: no cap) and the resulting residency.
+int residency_pad(const void *fn, int threads, int64_t blocks, int cus, int static_lds, int *resident) {
+    const int b = occupancy(fn, threads, 0);
+    *resident = b;
+    if (cus <= 0 || (b != 3 && b != 4))
+        return 0;
+    const int64_t n = (blocks + cus - 1) / cus;
+    if (n != b + 1)
+        return 0;
+    const int r = (int)((n + 1) / 2);
+    const int per_block = (kLdsBytes / r) / 2048 * 2048;
+    const int pad = per_block - static_lds;
+    if (pad <= 0 || pad > 65536 || occupancy(fn, threads, pad) != r)
+        return 0;
+    *resident = r;
+    return pad;
 }
 
 // ---- 16-bit GEMM -------------------------------------------------------------------
@@ -696,7 +743,11 @@ int mgemm_sgemm_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     g.gn = (int)((N + p.bn - 1) / p.bn);
     g.vec_store = aligned16(C) && ldc % 4 == 0;
     g.a_cols = (int)K;
-    return launch(select_gemm(p), p.blocks, &g, s, p.threads);
+    const void *fn = select_gemm(p);
+    int resident;
+    const int pad = residency_pad(fn, p.threads, p.blocks, g_cus[dev].load(std::memory_order_relaxed),
+                                  (int)p.lds_bytes, &resident);
+    return launch(fn, p.blocks, &g, s, p.threads, pad);
 }
 
 int mgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
@@ -805,10 +856,12 @@ int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K, const float *A, int64_t
     int dev;
     if ((st = current_device(&dev)) != MGEMM_OK)
         return st;
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, select_gemm(p), p.threads, 0) != hipSuccess)
+    const void *fn = select_gemm(p);
+    if (occupancy(fn, p.threads, 0) < 1)
         return MGEMM_ERR_LAUNCH;
-    *blocks_per_cu = occ;
+    int resident;
+    residency_pad(fn, p.threads, p.blocks, g_cus[dev].load(std::memory_order_relaxed), (int)p.lds_bytes, &resident);
+    *blocks_per_cu = resident;
     return MGEMM_OK;
 }
 

@@ -153,6 +153,20 @@ def test_blocks_per_cu_query():
         m.blocks_per_cu(64, 64, 64, stages=4, fill="sync")
 
 
+def test_residency_cap():
+    """Where every CU would take exactly one block more than the 3 or 4 it
+    holds, the launch holds half as many per CU, rounded up; elsewhere the
+    kernel's own residency stands. (Bit identity across residencies is the
+    4096^3 full-size test's.)"""
+    q = lambda M, N, K, **kw: m.blocks_per_cu(M, N, K, compute="mfma", tile="128x128", **kw)
+    assert q(8192, 8192, 8192, stages=3) == 3             # 16 blocks per CU: no cap
+    assert q(3072, 4096, 4096, stages=3) == 3             # 3 per CU: one round, no cap
+    assert q(4096, 4096, 4096, stages=3) == 2             # 4 per CU against 3 resident: two rounds of 2
+    assert q(3584, 4096, 4096, stages=3) == 2             # 896 blocks: up to 4 per CU
+    assert q(4608, 4096, 4096, stages=2, fill="sync") == 3  # 5 per CU against 4 resident
+    assert q(4096, 4096, 4096, stages=2, fill="sync") == 4  # 4 per CU: one round
+
+
 def test_b128_and_b32_loaders_agree_when_both_apply():
     M, N, K = 384, 256, 320
     A, B = _inputs("uniform", M, N, K, seed=20)
