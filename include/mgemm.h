@@ -224,7 +224,8 @@ int mgemm_plan_sgemm(int64_t M, int64_t N, int64_t K,
  * stage-depth study of "Day 74 -- Async copies and pipelines" (section
  * "Exercise": a deeper ring costs LDS per block and so resident blocks).
  * This includes the launch's residency cap: where every CU would take exactly
- * one block more than the 3 or 4 it holds, mgemm_sgemm_ex requests unused
+ * one block more than the 3 or 4 it holds (any tile but the 64x64 VALU one,
+ * which needs its resident waves for FMA issue), mgemm_sgemm_ex requests unused
  * dynamic LDS so that each CU holds half its blocks, rounded up (two even
  * rounds instead of a lockstep round and a lone block). Results do not depend on it.
  * Validates like mgemm_plan_sgemm, then queries the current device:

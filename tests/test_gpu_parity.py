@@ -165,6 +165,8 @@ def test_residency_cap():
     assert q(3584, 4096, 4096, stages=3) == 2             # 896 blocks: up to 4 per CU
     assert q(4608, 4096, 4096, stages=2, fill="sync") == 3  # 5 per CU against 4 resident
     assert q(4096, 4096, 4096, stages=2, fill="sync") == 4  # 4 per CU: one round
+    # the 64x64 VALU tile keeps its residency (3 at six stages, 4 blocks per CU at N = 2048)
+    assert m.blocks_per_cu(2048, 2048, 2048, stages=6, compute="valu", tile="64x64") == 3
 
 
 def test_b128_and_b32_loaders_agree_when_both_apply():
