@@ -159,6 +159,10 @@ def peak_clock_mhz():
     return round(v.value / 1000.0, 1)
 
 
+# blocks of 10 timed launches per table entry: the median and the minimum are reported
+REPEATS = 5
+
+
 def timed_launches(fn, warmup=3, runs=10, repeats=1):
     """The pages' protocol ("pipelined_gemm.cu", timeKernel): warm-up launches,
     then the mean of `runs` launches between two events; `repeats` blocks give
@@ -298,9 +302,10 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
                     if compute == "valu" and n > 4096 and (fill, S) not in (("sync", 1), ("piped", 2), ("piped", 3)):
                         continue
                     t = timed_launches(lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute,
-                                                       tile="128x128"), repeats=3)
+                                                       tile="128x128"), repeats=REPEATS)
                     row[f"{compute}_{fill}_S{S}"] = {
-                        "ms": round(t["ms_median"], 4), "gflops": round(flop / (t["ms_median"] * 1e-3) / 1e9, 1),
+                        "ms": round(t["ms_median"], 4), "ms_min": round(t["ms_min"], 4),
+                        "gflops": round(flop / (t["ms_median"] * 1e-3) / 1e9, 1),
                         "pct_peak": round(100 * flop / (t["ms_median"] * 1e-3) / 1e12 / 157.3, 2)}
         for compute in ("mfma", "valu"):
             base = row.get(f"{compute}_sync_S1")
@@ -328,13 +333,13 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
     for shape in COPY_VIEWS:
         view = f"{shape[0]}x{shape[1]}"
         for S in (1, 2, 3):
-            t = timed_launches(lambda: m.tile_copy(src.view(*shape), dst.view(*shape), stages=S), repeats=3)
+            t = timed_launches(lambda: m.tile_copy(src.view(*shape), dst.view(*shape), stages=S), repeats=REPEATS)
             gbs = nbytes / (t["ms_median"] * 1e-3) / 1e9
-            copy[f"{view}_S{S}"] = {"ms": round(t["ms_median"], 4), "GBps": round(gbs, 1),
+            copy[f"{view}_S{S}"] = {"ms": round(t["ms_median"], 4), "ms_min": round(t["ms_min"], 4), "GBps": round(gbs, 1),
                                     "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
         if not torch.equal(src, dst):
             raise SystemExit("tile copy changed bytes")
-    t = timed_launches(lambda: dst.copy_(src), repeats=3)
+    t = timed_launches(lambda: dst.copy_(src), repeats=REPEATS)
     copy["torch_copy_context"] = {"ms": round(t["ms_median"], 4),
                                   "GBps": round(nbytes / (t["ms_median"] * 1e-3) / 1e9, 1)}
     res["tile_copy_1GiB"] = copy
@@ -371,11 +376,11 @@ def gemm16_table(m, datagen, torch, sizes):
                 torch.cuda.synchronize()
                 if not torch.equal(C.view(torch.int32), C1.view(torch.int32)):
                     raise SystemExit(f"gemm16 parity gate: {fmt} {n} {tile} {fill} S{S} differs from sync S1")
-                t = timed_launches(lambda: m.gemm16(A, B, C, stages=S, fill=fill, tile=tile), repeats=3)
+                t = timed_launches(lambda: m.gemm16(A, B, C, stages=S, fill=fill, tile=tile), repeats=REPEATS)
                 tf = flop / (t["ms_median"] * 1e-3) / 1e12
                 row[f"{tile}_{fill}_S{S}"] = {"ms": round(t["ms_median"], 4), "tflops": round(tf, 1),
                                               "pct_peak": round(100 * tf / PEAK_16BIT_TFLOPS, 2)}
-            t = timed_launches(lambda: torch.matmul(A, B), repeats=3)
+            t = timed_launches(lambda: torch.matmul(A, B), repeats=REPEATS)
             row["torch_matmul_context"] = {"ms": round(t["ms_median"], 4),
                                            "tflops": round(flop / (t["ms_median"] * 1e-3) / 1e12, 1)}
             best = max((k for k in row if k != "torch_matmul_context"), key=lambda k: row[k]["tflops"])
@@ -416,11 +421,11 @@ def attention_table(m, datagen, torch):
                     torch.cuda.synchronize()
                     if not torch.equal(O.view(torch.int32), O1.view(torch.int32)):
                         raise SystemExit(f"attention parity gate: {fmt} D{D} {fill} S{St} differs from sync S1")
-                    t = timed_launches(lambda: m.attention(Q, K, V, O, stages=St, fill=fill), repeats=3)
+                    t = timed_launches(lambda: m.attention(Q, K, V, O, stages=St, fill=fill), repeats=REPEATS)
                     tf = flop / (t["ms_median"] * 1e-3) / 1e12
                     row[f"{fill}_S{St}"] = {"ms": round(t["ms_median"], 4), "tflops": round(tf, 1),
                                             "pct_peak": round(100 * tf / PEAK_16BIT_TFLOPS, 2)}
-            t = timed_launches(lambda: F.scaled_dot_product_attention(Q, K, V), repeats=3)
+            t = timed_launches(lambda: F.scaled_dot_product_attention(Q, K, V), repeats=REPEATS)
             row["torch_sdpa_context"] = {"ms": round(t["ms_median"], 4),
                                          "tflops": round(flop / (t["ms_median"] * 1e-3) / 1e12, 1)}
             row["best"] = max((k for k in row if k != "torch_sdpa_context"), key=lambda k: row[k]["tflops"])
@@ -444,12 +449,12 @@ def stage_study(m, torch, Ad8, Bd8, Cd8):
         flop = 2.0 * n ** 3
         rows = {}
         base = timed_launches(lambda: m.sgemm(A, B, C, stages=1, fill="sync", compute=compute, tile=tile),
-                              repeats=3)["ms_median"]
+                              repeats=REPEATS)["ms_median"]
         rows["sync_S1"] = {"ms": round(base, 4), "gflops": round(flop / base / 1e6, 1)}
         for fill in ("piped", "piped_ws"):
             for S in range(1, 7):
                 ms = timed_launches(lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute, tile=tile),
-                                    repeats=3)["ms_median"]
+                                    repeats=REPEATS)["ms_median"]
                 p = m.plan(n, n, n, stages=S, fill=fill, compute=compute, tile=tile)
                 rows[f"{fill}_S{S}"] = {"ms": round(ms, 4), "gflops": round(flop / ms / 1e6, 1),
                                         "piped_over_sync": round(ms / base, 3), "lds_bytes": p["lds_bytes"],
