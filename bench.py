@@ -321,6 +321,7 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
         if n != big:
             del A, B, C
     res["gemm"] = gemm
+    res["gemm_small"] = small_gemm_table(m, datagen, torch)
     res["stage_study"] = stage_study(m, torch, Ad8, Bd8, Cd8)
     res["gemm16"] = gemm16_table(m, datagen, torch, sorted({min(4096, big), big}))
     res["attention"] = attention_table(m, datagen, torch)
@@ -480,6 +481,40 @@ def cpu_baseline(Ad, Bd, budget_s=12.0):
     return {"value": round(fl / dt / 1e9, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {Ad.shape[0]} rows of the {Ad.shape[0]}x{Bd.shape[1]}x{Ad.shape[1]} product "
                       f"(fp64 accumulate), {dt:.1f} s wall"}
+
+
+def small_gemm_table(m, datagen, torch):
+    """The pages' own small shapes on the seeded U[-1,1) inputs: 256^3 with
+    their 64x64x16 tile (4x4 micro-tile, VALU), sync S=1 against piped S=2,
+    and 1024^3 at every fill and depth with the automatic tile (VALU and
+    MFMA). Each output is checked bitwise against the sync S=1 one first."""
+    out = {}
+    for n, cases in ((256, [("valu", "64x64", "sync", 1), ("valu", "64x64", "piped", 2)]),
+                     (1024, [(c, "auto", f, S) for c in ("valu", "mfma") for f in ("sync", "piped") for S in (1, 2, 3)])):
+        A = datagen.uniform_pm1_torch(datagen.SEED_A, n * n, device="cuda").view(n, n)
+        B = datagen.uniform_pm1_torch(datagen.SEED_B, n * n, device="cuda").view(n, n)
+        C = torch.empty((n, n), device="cuda")
+        flop = 2.0 * n ** 3
+        row, ref = {}, {}
+        for compute, tile, fill, S in cases:
+            f = lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute, tile=tile)
+            f()
+            torch.cuda.synchronize()
+            if compute not in ref:
+                ref[compute] = C.clone()
+            elif not torch.equal(C.view(torch.int32), ref[compute].view(torch.int32)):
+                raise SystemExit(f"bench: {n}^3 {compute} {fill} S={S} differs from sync S=1")
+            t = timed_launches(f, repeats=REPEATS)
+            row[f"{compute}_{tile}_{fill}_S{S}"] = {
+                "ms": round(t["ms_median"], 5), "ms_min": round(t["ms_min"], 5),
+                "gflops": round(flop / (t["ms_median"] * 1e-3) / 1e9, 1),
+                "pct_peak": round(100 * flop / (t["ms_median"] * 1e-3) / 1e12 / 157.3, 2)}
+        for key, v in row.items():
+            base = row[key.rsplit("_", 2)[0] + "_sync_S1"]
+            if "_piped_" in key:
+                v["speedup_vs_sync_S1"] = round(base["ms"] / v["ms"], 3)
+        out[str(n)] = row
+    return out
 
 
 def cpu_model():
