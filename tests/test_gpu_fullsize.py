@@ -55,6 +55,32 @@ def test_square_full_size(n):
         del ref, other
 
 
+@pytest.mark.parametrize("M", [3584, 4608])
+def test_residency_capped_grids(M):
+    """Grids where the launch caps residency (896 tiles: piped S=3 holds 2
+    blocks per CU instead of 3; 1152 tiles: sync S=2 holds 3 instead of 4):
+    every fill and depth stays bit-identical and within the bound on sampled
+    rows."""
+    N, K = 4096, 512
+    Ad = _dev_uniform(datagen.SEED_A, M, K)
+    Bd = _dev_uniform(datagen.SEED_B, K, N)
+    capped = {3584: ("piped", 3, 2), 4608: ("sync", 2, 3)}[M]
+    assert m.blocks_per_cu(M, N, K, stages=capped[1], fill=capped[0], compute="mfma", tile="128x128") == capped[2]
+    rows = _sample_rows(M)
+    for compute in ("mfma", "valu"):
+        ref = torch.empty((M, N), device="cuda")
+        m.sgemm(Ad, Bd, ref, stages=1, fill="sync", compute=compute, tile="128x128")
+        torch.cuda.synchronize()
+        check_bound(ref[torch.as_tensor(rows, device="cuda")].cpu().numpy(), _host_rows(Ad, rows), Bd.cpu().numpy(),
+                    what=f"{M}x{N}x{K} {compute} sync S=1 (sampled rows)")
+        other = torch.empty_like(ref)
+        for fill, S in (("sync", 2), ("sync", 3), ("piped", 1), ("piped", 2), ("piped", 3), ("piped", 4)):
+            other.fill_(float("nan"))
+            m.sgemm(Ad, Bd, other, stages=S, fill=fill, compute=compute, tile="128x128")
+            torch.cuda.synchronize()
+            assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), (M, compute, fill, S)
+
+
 def test_ragged_full_size():
     """M = 4099, N = 3001, K = 1537 with lda = 1537 and ldb = ldc = 3001: no
     leading dimension is a multiple of 4, so every fill takes 4-byte loads,
