@@ -431,7 +431,8 @@ struct AttnSyncOps : AttnCtx<Tile, W> {
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(this->k_ptr(sp));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(this->v_ptr(sp));
         // two register sets or more: one load form, kept ahead of the compute
-        // (as in the GEMM's register-staged ring)
+        // (as in the GEMM's register-staged ring; with the full-slice fast
+        // path as well, S=3 measured 668 -> 608 TFLOP/s at D = 64)
         if (NSET == 1 && __builtin_expect(rows >= kAttnBK, 1)) {
 #pragma unroll
             for (int i = 0; i < C::OK::U; ++i)

@@ -159,13 +159,12 @@ MG_HD inline void piped_schedule_split(int T, Ops &ops) {
 // With two sets or more the loop runs whole groups of S-1 iterations,
 // stopping before the last slice, so that register-set indices are
 // compile-time constants and every load, compute and store in its body is
-// unconditional (a load past the last
-// slice is the masked one, and its set is never stored). Conditional loads
-// or stores there made the compiler's wait counts assume the worst path and
-// drain the slice issued last before each store; a set index chosen at run
-// time made it copy the sets between branches; computes under a branch each
-// made it keep a second copy of the accumulators. The last 1 .. S-1 slices
-// run after the loop.
+// unconditional (a load past the last slice is the masked one, and its set
+// is never stored). Conditional loads or stores there made the compiler's
+// wait counts assume the worst path and drain the slice issued last before
+// each store; a set index chosen at run time made it copy the sets between
+// branches; computes under a branch each made it keep a second copy of the
+// accumulators. The last 1 .. S-1 slices run after the loop.
 template <int S, class Ops>
 MG_HD inline void sync_schedule(int T, Ops &ops) {
     static_assert(S >= 1 && S <= kMaxSyncStages, "stages must be 1, 2 or 3");
