@@ -24,6 +24,23 @@ def test_pin(lib, pin):
     pin(lib)
 
 
+def test_thread_count_does_not_change_results(lib):
+    """Each output row is one thread's sequential sum, so the oracle's thread
+    count (set for timing) changes no bit of its result."""
+    import datagen
+    A = datagen.matrix("uniform", 41, 37, 53)
+    B = datagen.matrix("uniform", 42, 53, 29)
+    threads = oracle.num_threads(lib)
+    try:
+        oracle.set_threads(1, lib)
+        assert oracle.num_threads(lib) == 1
+        one = oracle.gemm_f64(A, B)
+    finally:
+        oracle.set_threads(threads, lib)
+    assert oracle.num_threads(lib) == threads
+    assert oracle.gemm_f64(A, B).tobytes() == one.tobytes()
+
+
 def test_bound_formula():
     # slack 4, K terms, unit roundoff 2^-24 of fp32 round-to-nearest
     Abs = np.array([[1.0, 2.0]])
