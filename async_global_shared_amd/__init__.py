@@ -181,7 +181,16 @@ def _mat(t, name):
         raise TypeError(f"{name} must be on a GPU")
     if t.numel() and t.stride(1) != 1:
         raise TypeError(f"{name} must have unit column stride")
-    return t.data_ptr(), max(t.stride(0), t.shape[1])
+    return t.data_ptr(), _ld(t)
+
+
+def _ld(t):
+    """The row stride passed as the leading dimension. A single row has no
+    meaningful stride (the width stands in); with two rows or more the
+    stride goes through as it is, so an overlapping view (an expanded row,
+    stride 0, or any stride below the width) reaches the C ABI's ld < cols
+    check and is refused before any launch."""
+    return max(t.stride(0), t.shape[1]) if t.shape[0] <= 1 else t.stride(0)
 
 
 def _stream(stream):
@@ -220,7 +229,7 @@ def _mat16(t, name):
         raise TypeError(f"{name} must be on a GPU")
     if t.numel() and t.stride(1) != 1:
         raise TypeError(f"{name} must have unit column stride")
-    return t.data_ptr(), max(t.stride(0), t.shape[1])
+    return t.data_ptr(), _ld(t)
 
 
 def gemm16(A, B, C=None, *, stages: int = 2, fill: str = "piped", tile: str = "auto", stream=None):

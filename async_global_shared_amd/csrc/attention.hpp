@@ -1,7 +1,8 @@
 // attention.hpp -- scaled dot-product attention forward on the asynchronous
 // K/V ring, for gfx950 (CDNA4).
 //
-// "A study on CUDA async memcpy", the FlashAttention tile pipeline section:
+// The async copy article ("from cp.async to memcpy_async"), section 6.2,
+// "FlashAttention's tile pipeline":
 // a block keeps its Q tile for the whole loop, the K/V tiles stream through
 // the LDS ring (the next one in flight while the current one is scored), and
 // each step rescales and accumulates the running result (the online

@@ -512,6 +512,26 @@ Range span4(const void *p, int64_t batch, int64_t heads, int64_t rows, int64_t c
     return r;
 }
 
+// Every element of a strided view has its own address: with the
+// dimensions of extent > 1 taken in order of stride, each stride exceeds the
+// furthest offset the smaller ones reach. (A sufficient test; it accepts
+// every permuted dense layout, e.g. (batch, seq, head, dim) storage.)
+bool disjoint_view(int n, const int64_t *size, const int64_t *stride) {
+    std::pair<int64_t, int64_t> dims[8]; // (stride, extent) of the dimensions with extent > 1
+    int k = 0;
+    for (int i = 0; i < n && i < 8; ++i)
+        if (size[i] > 1)
+            dims[k++] = {stride[i], size[i]};
+    std::sort(dims, dims + k);
+    int64_t reach = 0; // furthest offset the dimensions taken so far reach
+    for (int i = 0; i < k; ++i) {
+        if (dims[i].first <= reach)
+            return false;
+        reach += dims[i].first * (dims[i].second - 1);
+    }
+    return true;
+}
+
 struct AttnView {
     const void *p;
     int64_t sb, sh, ld;
@@ -558,6 +578,10 @@ int plan_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, i
             return MGEMM_ERR_ARG;
         if (o.ld >= kMaxLd)
             return MGEMM_ERR_UNSUPPORTED;
+        // distinct (batch, head, query, column) outputs need distinct addresses
+        const int64_t osize[4] = {batch, heads, seq_q, D}, ostride[4] = {o.sb, o.sh, o.ld, 1};
+        if (!disjoint_view(4, osize, ostride))
+            return MGEMM_ERR_ALIAS;
         const int64_t nqb = (seq_q + kAttnBQ - 1) / kAttnBQ;
         if (seq_q >= kMaxExtent || seq_k >= kMaxExtent || batch * heads >= kMaxExtent ||
             batch * heads * nqb >= kMaxExtent)

@@ -239,3 +239,76 @@ def matrix16(seed: int, rows: int, cols: int, fmt: str, kind: str = "grid", ld: 
     out = np.full((rows, ld), 0x7FC0 if fmt == "bf16" else 0x7E00, dtype=np.uint16)
     out[:, :cols] = to_bits16(v, fmt).reshape(rows, cols)
     return out
+
+
+# ---- structured attention inputs (full-size slice checks) --------------------
+#
+# Patterns, not draws: every value is a small integer or +-1, exact in both
+# 16-bit formats. They are built with torch on any device (the full-size
+# tensors are large) and returned as float32; callers cast to bfloat16 or
+# float16, which changes no value.
+
+def attn_slice_sentinel_v(batch: int, heads: int, seq: int, dim: int, group: int = 64, device="cpu"):
+    """V[b, h, j, c] = floor(j / group) + ((c + 7 h + 3 b) mod dim).
+
+    Integers below 2^8 for seq <= 64 group and dim <= 128 (exact in
+    bfloat16 and binary16); with uniform weights the mean over keys of a
+    column is a closed form, and a skipped or repeated group of keys moves
+    it."""
+    import torch
+    j = torch.arange(seq, device=device, dtype=torch.int64) // group
+    c = torch.arange(dim, device=device, dtype=torch.int64)
+    b = torch.arange(batch, device=device, dtype=torch.int64)[:, None]
+    h = torch.arange(heads, device=device, dtype=torch.int64)[None, :]
+    r = (c[None, None, :] + 7 * h[..., None] + 3 * b[..., None]) % dim  # (batch, heads, dim)
+    return (j[None, None, :, None] + r[:, :, None, :]).to(torch.float32)
+
+
+def attn_peaked_winner(batch: int, heads: int, seq_q: int, group: int = 64, groups: int = 64, device="cpu"):
+    """Key index w[b, h, i] = group * a + t that query i of head (b, h) is
+    built to single out: a = (i + 5 h + 11 b) mod groups (its group of keys),
+    t = (floor(i / groups) + 3 h + b) mod group (its place in the group). For
+    seq_q = groups * group every key of a head is some query's winner once."""
+    import torch
+    i = torch.arange(seq_q, device=device, dtype=torch.int64)[None, None, :]
+    b = torch.arange(batch, device=device, dtype=torch.int64)[:, None, None]
+    h = torch.arange(heads, device=device, dtype=torch.int64)[None, :, None]
+    a = (i + 5 * h + 11 * b) % groups
+    t = (i // groups + 3 * h + b) % group
+    return group * a + t
+
+
+def _pm1_code(x, half):
+    """(position, sign) of the signed one-hot code of x in [0, 2 half):
+    position x mod half, sign +1 below half and -1 from half on."""
+    import torch
+    return x % half, torch.where(x < half, 1.0, -1.0)
+
+
+def attn_peaked_qk(batch: int, heads: int, seq_q: int, seq_k: int, dim: int, group: int = 64, groups: int = 64,
+                   device="cpu"):
+    """(Q, K) as float32 (batch, heads, seq, dim) tensors of 0 and +-1.
+
+    Key j = group * s + t carries the signed one-hot code of t (in dims
+    0 .. group/2 - 1) and of s (in dims group/2 .. group - 1); query i carries
+    the codes of its winner attn_peaked_winner(...)[b, h, i]. The dot product
+    is +2 for the winner and at most +1 for every other key (each code
+    contributes +1 on a match, 0 or -1 otherwise). Needs dim >= group,
+    seq_k <= group * groups and groups <= group."""
+    import torch
+    half = group // 2
+    if dim < group or seq_k > group * groups or groups > group:
+        raise ValueError("peaked pattern needs dim >= group, seq_k <= group * groups, groups <= group")
+    j = torch.arange(seq_k, device=device, dtype=torch.int64)
+    K = torch.zeros((seq_k, dim), device=device, dtype=torch.float32)
+    pt, st = _pm1_code(j % group, half)
+    ps, ss = _pm1_code(j // group, half)
+    K[j, pt] = st
+    K[j, half + ps] = ss
+    w = attn_peaked_winner(batch, heads, seq_q, group, groups, device=device)  # (batch, heads, seq_q)
+    Q = torch.zeros((batch, heads, seq_q, dim), device=device, dtype=torch.float32)
+    qt, qst = _pm1_code(w % group, half)
+    qs, qss = _pm1_code(w // group, half)
+    Q.scatter_(3, qt[..., None], qst[..., None])
+    Q.scatter_(3, (half + qs)[..., None], qss[..., None])
+    return Q, K.expand(batch, heads, seq_k, dim)

@@ -88,6 +88,11 @@ struct mgemm_plan; /* defined below (mgemm_plan_t) */
  * automatic tile and loader choice. For a fixed (shape, compute, tile), every
  * (stages, fill_mode, loader) gives bit-identical C. M == 0 or N == 0: no-op.
  * K == 0: C[0:M, 0:N] = +0. Cells of C outside M x N are never written.
+ * MGEMM_FILL_PIPED_WS guards each of its LDS-counter waits with a bounded
+ * spin (about 2^22 polls); a block whose wait runs out, which a correct
+ * protocol never lets happen, stops and writes NaN to its whole C tile.
+ * That is the only report: the call has already returned MGEMM_OK, so a
+ * caller that must tell such a failure from NaN in the data checks C.
  */
 int mgemm_sgemm(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda,
@@ -137,8 +142,9 @@ int mgemm_plan_gemm16(int64_t M, int64_t N, int64_t K,
                       struct mgemm_plan *plan);
 
 /*
- * Scaled dot-product attention forward ("A study on CUDA async memcpy", the
- * FlashAttention tile pipeline section: the Q tile stays put, K/V tiles
+ * Scaled dot-product attention forward (the async copy article, "from
+ * cp.async to memcpy_async", section 6.2 "FlashAttention's tile pipeline":
+ * the Q tile stays put, K/V tiles
  * stream through the asynchronous LDS ring while the current one is scored,
  * and each step rescales and accumulates the running output):
  *   O[b,h,i,:] = sum_j w_ij V[b,h,j,:],
@@ -155,7 +161,9 @@ int mgemm_plan_gemm16(int64_t M, int64_t N, int64_t K,
  * seq_k >= 1 whenever there is a query (softmax over no keys is undefined),
  * finite scale, stages 1 .. 4 (piped) or 1 .. 3 (sync), fill_mode
  * MGEMM_FILL_SYNC or MGEMM_FILL_PIPED (bit-identical results). O must not
- * overlap Q, K or V (MGEMM_ERR_ALIAS). batch, heads or seq_q == 0 is a no-op.
+ * overlap Q, K or V, and distinct (b, h, i, d) outputs must have distinct
+ * addresses (else MGEMM_ERR_ALIAS; any permuted dense layout qualifies).
+ * batch, heads or seq_q == 0 is a no-op.
  */
 int mgemm_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
                     const void *Q, int64_t q_sb, int64_t q_sh, int64_t q_ld,

@@ -213,7 +213,7 @@ def attention_f64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, fmt: str, scale: 
 
 def attention_bound(ref: AttnRef, fmt: str, scale: float) -> np.ndarray:
     """Acceptance bound of the attention kernels, elementwise:
-    (e_p + 4 delta_i) sum_j w_j |v_jc| + Sk 2^-125 max_j |v_jc|.
+    (e_p + 4 delta_i) sum_j w_j |v_jc| + Sk tau max_j |v_jc|.
     e_p = 2^-6 (bfloat16) or 2^-8 (binary16): the probabilities are rounded
     to the 16-bit format before the P V product (unit roundoff 2^-8 or
     2^-11), which moves each weight by at most about twice that, with fp32
@@ -223,10 +223,14 @@ def attention_bound(ref: AttnRef, fmt: str, scale: float) -> np.ndarray:
     the exponent and the shift by the row maximum); perturbing every score by
     at most delta moves each softmax weight by a factor within
     exp(+-2 delta), so O by at most 2 delta sum_j w_j |v_jc|, taken twice.
-    The last term covers underflow: the kernels' probabilities lie in [0, 1]
-    with a row sum of at least 1 (the row maximum contributes 2^0), and a
-    probability or rescaling factor below fp32's normal range (2^-126) drops
-    at most 2^-126 |v_jc| per key."""
+    The last term covers probabilities too small for a relative error: the
+    kernels' probabilities lie in [0, 1] with a row sum of at least 1 (the
+    row maximum contributes 2^0), and each key's rounded probability is off
+    by at most tau in absolute terms below the format's normal range. For
+    bfloat16 (fp32's exponent range) that is fp32 underflow, tau = 2^-125;
+    binary16 stops at subnormals spaced 2^-24 (nothing below 2^-25 survives
+    the rounding), so tau = 2^-25."""
     e_p = 2.0 ** -6 if fmt == "bf16" else 2.0 ** -8
+    tau = 2.0 ** -125 if fmt == "bf16" else 2.0 ** -25
     delta = abs(scale) * (ref.D + 8) * 2.0 ** -24 * ref.G
-    return (e_p + 4.0 * delta[..., None]) * ref.Wabs + ref.Sk * 2.0 ** -125 * ref.Vmax[..., None, :]
+    return (e_p + 4.0 * delta[..., None]) * ref.Wabs + ref.Sk * tau * ref.Vmax[..., None, :]

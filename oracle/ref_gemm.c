@@ -173,7 +173,8 @@ void oracle_gemm16_f64(int64_t M, int64_t N, int64_t K,
 }
 
 /* ---- scaled dot-product attention over 16-bit Q, K, V --------------------
- * "A study on CUDA async memcpy" (the FlashAttention tile pipeline section):
+ * The async copy article ("from cp.async to memcpy_async"), section 6.2,
+ * "FlashAttention's tile pipeline":
  * Q tiles stay put while K/V tiles stream past them, each step scoring the
  * current K tile, rescaling the running result and accumulating V. That
  * online form reaches, up to rounding, the plain definition written here:

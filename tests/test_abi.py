@@ -846,6 +846,38 @@ def test_attention_validation(kw, want):
                                  a["O"], *o, 0.125, a["dtype"], a["stages"], a["fill"], None) == want
 
 
+@pytest.mark.parametrize("o,want", [
+    ((3 * 100 * 64, 0, 64), m.ERR_ALIAS),           # every head writes the same rows
+    ((0, 100 * 64, 64), m.ERR_ALIAS),               # every batch writes the same rows
+    ((3 * 100 * 64, 100 * 64, 32), m.ERR_ARG),      # rows overlap (ld < head_dim)
+    ((3 * 100 * 64, 99 * 64, 64), m.ERR_ALIAS),     # a head's last row is the next head's first
+    ((100 * 3 * 64, 64, 3 * 64), m.OK),             # (batch, seq, head, dim) storage
+    ((3 * 64, 64, 2 * 3 * 64), m.OK),               # batch innermost of the rows: still disjoint
+    ((3 * (100 * 64 + 5) + 7, 100 * 64 + 5, 64), m.OK),  # padded strides
+    ((3 * 100 * 64 + 7, 100 * 64 + 5, 64), m.ERR_ALIAS),  # padded heads spill into the next batch
+])
+def test_attention_refuses_an_output_that_overlaps_itself(o, want):
+    st, _ = att(o=o)
+    assert st == want
+    if want != m.OK:  # refused by the launching entry point too, before any HIP call
+        assert m.mgemm_attention(2, 3, 100, 90, 64, A0, 3 * 100 * 64, 100 * 64, 64, B0, 3 * 90 * 64, 90 * 64, 64,
+                                 B0 + (1 << 24), 3 * 90 * 64, 90 * 64, 64, C0, *o, 0.125, 1, 2, 1, None) == want
+
+
+def test_overlapping_tensor_views_reach_the_ld_check():
+    """The binding passes a row stride below the width (an expanded row,
+    stride 0) through as the leading dimension, so the library refuses the
+    view (ld < cols) before any launch; a single row keeps its width."""
+    import torch
+    row = torch.ones(1, 8)
+    assert m._ld(row.expand(5, 8)) == 0
+    assert m._ld(torch.ones(6, 8).as_strided((3, 8), (4, 1))) == 4
+    assert m._ld(row) == 8 and m._ld(torch.ones(4, 8)[:, :5]) == 8
+    assert sg(lda=0) == m.ERR_ARG and sg(lda=4, K=8, M=3) == m.ERR_ARG and sg(ldc=0) == m.ERR_ARG
+    assert m.mgemm_tile_copy(5, 8, A0, 0, B0, 8, 2, None) == m.ERR_ARG
+    assert m.mgemm_gemm16(5, 8, 8, A0, 0, B0, 8, C0, 8, 1, 2, 1, 0, None) == m.ERR_ARG
+
+
 def test_attention_rejects_nonfinite_scale():
     for s in (float("nan"), float("inf"), float("-inf")):
         assert m.mgemm_attention(1, 1, 8, 8, 64, A0, 512, 512, 64, B0, 512, 512, 64, B0 + 4096, 512, 512, 64,

@@ -1,8 +1,10 @@
 """Parity of the attention kernels with the oracle, through the C ABI:
-|O - O_ref| <= (e_p + 4 delta_i) sum_j w_j |v_jc| + Sk 2^-125 max_j |v_jc|
+|O - O_ref| <= (e_p + 4 delta_i) sum_j w_j |v_jc| + Sk tau max_j |v_jc|
 elementwise (e_p = 2^-6 for bfloat16, 2^-8 for binary16: the probabilities'
 rounding; delta_i = |scale| (D + 8) 2^-24 max_j sum_d |q_id||k_jd|: the
-scores' fp32 rounding; the last term: weights below fp32's range),
+scores' fp32 rounding; tau = 2^-125 for bfloat16 (fp32 underflow), 2^-25 for
+binary16 (its smallest subnormal spacing, halved): weights too small for a
+relative error),
 bit-identical across fills and ring depths, O's padding untouched. Inputs: the 16-bit seeded grid generator (values on the format's
 grid in [-1, 1))."""
 import numpy as np
@@ -199,3 +201,74 @@ def test_full_size(fmt):
         assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), (fmt, fill, St)
     rows = np.unique(np.r_[0, 1, 127, 128, S - 1, np.linspace(0, S - 1, 10).astype(int)])
     check(ref, Q, K, V, fmt, D ** -0.5, f"{fmt} full size", heads=[(0, 0), (7, 11), (15, 15)], rows=rows)
+
+
+# ---- full-size slice sentinels -------------------------------------------------------
+# At B = H = 16, Sq = Sk = 4096 a skipped or repeated 64-key slice stays inside
+# the bound on seeded random inputs (the bound scales with the output's own
+# size), so two structured inputs check every slice at that size instead; the
+# CPU tests in test_attention_bound.py show that the oracle reproduces both
+# closed forms and that a kernel which drops or repeats one slice misses them.
+
+FULL_B, FULL_H, FULL_S = 16, 16, 4096
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [128, 64])
+def test_full_size_uniform_slice_sentinel(fmt, D):
+    """scale 0 (every weight 1/4096) and V[b, h, j, c] = floor(j/64) + r with
+    r = (c + 7h + 3b) mod D: every output is exactly 31.5 + r, on the whole
+    output, for every fill and depth."""
+    B, H, S = FULL_B, FULL_H, FULL_S
+    Q, K = dev_qkv(41, B, H, S, D, fmt), dev_qkv(42, B, H, S, D, fmt)
+    V = datagen.attn_slice_sentinel_v(B, H, S, D, device="cuda").to(TORCH16[fmt])
+    c = torch.arange(D, device="cuda")
+    r = (c[None, None, :] + 7 * torch.arange(H, device="cuda")[None, :, None] +
+         3 * torch.arange(B, device="cuda")[:, None, None]) % D
+    want = (31.5 + r.to(torch.float32))[:, :, None, :].expand(B, H, S, D)
+    O = torch.empty((B, H, S, D), device="cuda")
+    for fill, St in VARIANTS:
+        if not fits(St, fill, D):
+            continue
+        print(f"uniform slice sentinel {fmt} D={D} {fill} S={St}", flush=True)
+        O.fill_(float("nan"))
+        m.attention(Q, K, V, O, scale=0.0, stages=St, fill=fill)
+        torch.cuda.synchronize()
+        assert torch.equal(O, want), (fmt, D, fill, St)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [128, 64])
+def test_full_size_peaked_winner(fmt, D):
+    """Each query's winning key scores 2 and every other key at most 1
+    (datagen.attn_peaked_qk); at scale 30 the output is the winner's V row
+    to within 2^-22 relative (+1e-9). Over a head's 4096 queries every key
+    wins once, so a slice read from the wrong slot or skipped changes whole
+    output rows. Whole output, every fill and depth; bit identity across
+    them; sampled heads and rows against the oracle's bound."""
+    B, H, S = FULL_B, FULL_H, FULL_S
+    scale = 30.0
+    Qf, Kf = datagen.attn_peaked_qk(B, H, S, S, D, device="cuda")
+    Q, K = Qf.to(TORCH16[fmt]), Kf.to(TORCH16[fmt]).contiguous()
+    del Qf, Kf
+    V = dev_qkv(43, B, H, S, D, fmt)
+    w = datagen.attn_peaked_winner(B, H, S, device="cuda")
+    Vw = torch.gather(V.float(), 2, w[..., None].expand(B, H, S, D))
+    tol = 2.0 ** -22 * Vw.abs() + 1e-9
+    O = torch.empty((B, H, S, D), device="cuda")
+    ref = None
+    for fill, St in VARIANTS:
+        if not fits(St, fill, D):
+            continue
+        print(f"peaked winner {fmt} D={D} {fill} S={St}", flush=True)
+        O.fill_(float("nan"))
+        m.attention(Q, K, V, O, scale=scale, stages=St, fill=fill)
+        torch.cuda.synchronize()
+        bad = ~((O - Vw).abs() <= tol)
+        assert not bool(bad.any()), (fmt, D, fill, St, int(bad.sum()))
+        if ref is None:
+            ref = O.clone()
+        else:
+            assert torch.equal(O.view(torch.int32), ref.view(torch.int32)), (fmt, D, fill, St)
+    rows = np.array([0, 1, 63, 64, 2047, S - 1])
+    check(ref, Q, K, V, fmt, scale, f"{fmt} D={D} peaked", heads=[(0, 0), (9, 5)], rows=rows)

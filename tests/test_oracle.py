@@ -47,17 +47,6 @@ def test_bound_formula():
     assert np.array_equal(oracle.bound(1024, Abs), 4 * 1024 * 2.0 ** -24 * Abs)
 
 
-def test_attention_bound_formula():
-    W = np.array([[1.0, 0.5]])
-    G = np.array([3.0])
-    Vm = np.array([2.0, 4.0])
-    ref = oracle.AttnRef(np.zeros_like(W), W, G, Vm, 64, 10)
-    floor = 10 * 2.0 ** -125 * Vm
-    b = oracle.attention_bound(ref, "bf16", -2.0)
-    assert np.allclose(b, (2.0 ** -6 + 4 * 2.0 * 72 * 2.0 ** -24 * 3.0) * W + floor, rtol=1e-15, atol=0)
-    assert np.allclose(oracle.attention_bound(ref, "f16", 0.0), 2.0 ** -8 * W + floor, rtol=1e-15, atol=0)
-
-
 # Deliberate mistakes planted in copies of the oracle's source. Each must be
 # caught by at least one pin, which shows the pins can see that class of bug.
 MUTANTS = {
