@@ -255,8 +255,12 @@ def main():
         "plan": plan,
     }
 
+    clock = extra["peak_clock_mhz"]
+    if clock:
+        # 256 FLOP per clock per CU: 4 SIMDs, each a 32x32x2 fp32 MFMA (4096 FLOP) every 64 clocks
+        extra["peak_fp32_tflops_from_device"] = round(props.multi_processor_count * 256 * clock / 1e6, 1)
     if not args.no_extra:
-        extra.update(tables(m, datagen, torch, Ad, Bd, Cd))
+        extra.update(tables(m, datagen, torch, Ad, Bd, Cd, with_oracle=not args.no_cpu))
 
     cpu = None
     if not args.no_cpu:
@@ -284,7 +288,43 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def tables(m, datagen, torch, Ad8, Bd8, Cd8):
+class Gate:
+    """Bitwise parity gate of a table: the first variant run becomes the
+    reference output and every later variant must reproduce it bit for bit
+    before it is timed (the pages' program compares the piped output with
+    the synchronous one before timing either, "pipelined_gemm.cu", main)."""
+
+    def __init__(self, torch, what):
+        self.torch, self.what, self.ref = torch, what, None
+
+    def check(self, run, out, variant):
+        torch = self.torch
+        out.fill_(float("nan"))
+        run()
+        torch.cuda.synchronize()
+        if self.ref is None:
+            self.ref = out.clone()
+        elif not torch.equal(out.view(torch.int32), self.ref.view(torch.int32)):
+            raise SystemExit(f"bench parity gate: {self.what} {variant} differs from the first variant")
+
+
+def oracle_rate(Ad, Bd, budget_s=3.0):
+    """The oracle (fp64, OpenMP over rows, all host threads) on the same
+    inputs: as many leading rows of A as fit about `budget_s` of wall time
+    (all of them for the smaller problems), in GFLOP/s."""
+    import oracle
+    lib = oracle.load()
+    threads = oracle.num_threads(lib)
+    B_host = Bd.cpu().numpy()
+    M = Ad.shape[0]
+    probe = min(M, threads)
+    dt, _ = oracle.timed_gemm_rows(Ad[:probe].cpu().numpy(), B_host, probe, lib=lib)
+    rows = int(min(M, max(probe, probe * int(budget_s / max(dt, 1e-4)))))
+    dt, fl = oracle.timed_gemm_rows(Ad[:rows].cpu().numpy(), B_host, rows, lib=lib)
+    return {"gflops": round(fl / dt / 1e9, 3), "threads": threads, "rows": rows, "of_rows": M, "s": round(dt, 3)}
+
+
+def tables(m, datagen, torch, Ad8, Bd8, Cd8, with_oracle=True):
     """Stage/fill table (GFLOP/s, speedups), VALU variant, tile copy GB/s."""
     res = {}
     gemm = {}
@@ -297,12 +337,14 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
         flop = 2.0 * n ** 3
         row = {}
         for compute in ("mfma", "valu"):
+            gate = Gate(torch, f"{n}^3 {compute} 128x128")
             for fill in ("sync", "piped"):
                 for S in (1, 2, 3):
                     if compute == "valu" and n > 4096 and (fill, S) not in (("sync", 1), ("piped", 2), ("piped", 3)):
                         continue
-                    t = timed_launches(lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute,
-                                                       tile="128x128"), repeats=REPEATS)
+                    run = lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute, tile="128x128")
+                    gate.check(run, C, f"{fill} S={S}")
+                    t = timed_launches(run, repeats=REPEATS)
                     row[f"{compute}_{fill}_S{S}"] = {
                         "ms": round(t["ms_median"], 4), "ms_min": round(t["ms_min"], 4),
                         "gflops": round(flop / (t["ms_median"] * 1e-3) / 1e9, 1),
@@ -317,11 +359,14 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8):
                     p["time_ratio_piped_over_sync_S1"] = round(p["ms"] / base["ms"], 3)
                 if s and p:
                     p["speedup_vs_sync_same_S"] = round(s["ms"] / p["ms"], 3)
+        if with_oracle and n != big:  # the full size's oracle rate is the cpu_baseline record
+            row["oracle"] = oracle_rate(A, B)
         gemm[str(n)] = row
         if n != big:
             del A, B, C
     res["gemm"] = gemm
-    res["gemm_small"] = small_gemm_table(m, datagen, torch)
+    res["gemm_small"] = small_gemm_table(m, datagen, torch, with_oracle)
+    res["gemm_ragged_tall_skinny"] = config5_table(m, datagen, torch, with_oracle)
     res["stage_study"] = stage_study(m, torch, Ad8, Bd8, Cd8)
     res["gemm16"] = gemm16_table(m, datagen, torch, sorted({min(4096, big), big}))
     res["attention"] = attention_table(m, datagen, torch)
@@ -449,16 +494,21 @@ def stage_study(m, torch, Ad8, Bd8, Cd8):
             C = torch.empty((n, n), device="cuda")
         flop = 2.0 * n ** 3
         rows = {}
-        base = timed_launches(lambda: m.sgemm(A, B, C, stages=1, fill="sync", compute=compute, tile=tile),
-                              repeats=REPEATS)["ms_median"]
+        gate = Gate(torch, f"stage study {name}")
+        run = lambda: m.sgemm(A, B, C, stages=1, fill="sync", compute=compute, tile=tile)
+        gate.check(run, C, "sync S=1")
+        base = timed_launches(run, repeats=REPEATS)["ms_median"]
         rows["sync_S1"] = {"ms": round(base, 4), "gflops": round(flop / base / 1e6, 1)}
         for fill in ("piped", "piped_ws"):
             for S in range(1, 7):
-                ms = timed_launches(lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute, tile=tile),
-                                    repeats=REPEATS)["ms_median"]
+                run = lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute, tile=tile)
+                gate.check(run, C, f"{fill} S={S}")
+                ms = timed_launches(run, repeats=REPEATS)["ms_median"]
                 p = m.plan(n, n, n, stages=S, fill=fill, compute=compute, tile=tile)
                 rows[f"{fill}_S{S}"] = {"ms": round(ms, 4), "gflops": round(flop / ms / 1e6, 1),
-                                        "piped_over_sync": round(ms / base, 3), "lds_bytes": p["lds_bytes"],
+                                        "speedup_vs_sync_S1": round(base / ms, 3),
+                                        "time_ratio_piped_over_sync_S1": round(ms / base, 3),
+                                        "lds_bytes": p["lds_bytes"],
                                         "blocks_per_cu": m.blocks_per_cu(n, n, n, stages=S, fill=fill,
                                                                          compute=compute, tile=tile)}
         out[name] = rows
@@ -483,7 +533,7 @@ def cpu_baseline(Ad, Bd, budget_s=12.0):
                       f"(fp64 accumulate), {dt:.1f} s wall"}
 
 
-def small_gemm_table(m, datagen, torch):
+def small_gemm_table(m, datagen, torch, with_oracle=True):
     """The pages' own small shapes on the seeded U[-1,1) inputs: 256^3 with
     their 64x64x16 tile (4x4 micro-tile, VALU), sync S=1 against piped S=2,
     and 1024^3 at every fill and depth with the automatic tile (VALU and
@@ -513,7 +563,54 @@ def small_gemm_table(m, datagen, torch):
             base = row[key.rsplit("_", 2)[0] + "_sync_S1"]
             if "_piped_" in key:
                 v["speedup_vs_sync_S1"] = round(base["ms"] / v["ms"], 3)
+                v["time_ratio_piped_over_sync_S1"] = round(v["ms"] / base["ms"], 3)
+        if with_oracle:
+            row["oracle"] = oracle_rate(A, B)
         out[str(n)] = row
+    return out
+
+
+CONFIG5 = (("ragged_4099x3001x1537", 4099, 3001, 1537), ("tall_skinny_16384x64x4096", 16384, 64, 4096))
+CONFIG5_VARIANTS = (("sync", 1), ("sync", 2), ("sync", 3), ("piped", 1), ("piped", 2), ("piped", 3))
+
+
+def config5_table(m, datagen, torch, with_oracle=True):
+    """The ragged 4099x3001x1537 GEMM (lda = 1537, ldb = ldc = 3001: every
+    row misaligned for 16-byte loads, so 4-byte loads and zero-filled edge
+    tiles) and the tall-skinny 16384x64x4096 GEMM, on seeded U[-1,1) inputs
+    with the automatic tile: GFLOP/s and share of the fp32 peak per compute
+    tile, fill and ring depth, each variant bit-identical to the first (sync
+    S=1) before it is timed; speedups against sync S=1; the oracle's rate on
+    the same inputs."""
+    out = {}
+    for name, M, N, K in CONFIG5:
+        A = datagen.uniform_pm1_torch(datagen.SEED_A, M * K, device="cuda").view(M, K)
+        B = datagen.uniform_pm1_torch(datagen.SEED_B, K * N, device="cuda").view(K, N)
+        C = torch.empty((M, N), device="cuda")
+        flop = 2.0 * M * N * K
+        row = {}
+        for compute in ("valu", "mfma"):
+            plan = m.plan(M, N, K, compute=compute, stages=2, fill="piped")
+            gate = Gate(torch, f"{name} {compute}")
+            for fill, S in CONFIG5_VARIANTS:
+                run = lambda: m.sgemm(A, B, C, stages=S, fill=fill, compute=compute)
+                gate.check(run, C, f"{fill} S={S}")
+                t = timed_launches(run, repeats=REPEATS)
+                row[f"{compute}_{fill}_S{S}"] = {
+                    "ms": round(t["ms_median"], 5), "ms_min": round(t["ms_min"], 5),
+                    "gflops": round(flop / (t["ms_median"] * 1e-3) / 1e9, 1),
+                    "pct_peak": round(100 * flop / (t["ms_median"] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 2)}
+            base = row[f"{compute}_sync_S1"]["ms"]
+            for fill, S in CONFIG5_VARIANTS:
+                v = row[f"{compute}_{fill}_S{S}"]
+                if (fill, S) != ("sync", 1):
+                    v["speedup_vs_sync_S1"] = round(base / v["ms"], 3)
+                    v["time_ratio_over_sync_S1"] = round(v["ms"] / base, 3)
+            row[f"{compute}_plan"] = {k: plan[k] for k in ("tile", "bm", "bn", "blocks", "load_bytes")}
+        if with_oracle:
+            row["oracle"] = oracle_rate(A, B)
+        out[name] = row
+        del A, B, C
     return out
 
 

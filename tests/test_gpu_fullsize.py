@@ -55,6 +55,22 @@ def test_square_full_size(n):
         del ref, other
 
 
+def test_whole_output_8192_against_oracle():
+    """The benchmark's timed configuration (MFMA compute tile, 128x128,
+    piped S=2) on the full 8192^3 problem: every element of C against the
+    oracle's bound, as the pages' program checks every element against its
+    CPU product ("pipelined_gemm.cu", main). The oracle runs the whole fp64
+    product and |A||B| on the host cores (about 30 s)."""
+    n = 8192
+    Ad = _dev_uniform(datagen.SEED_A, n, n)
+    Bd = _dev_uniform(datagen.SEED_B, n, n)
+    C = torch.empty((n, n), device="cuda")
+    m.sgemm(Ad, Bd, C, stages=2, fill="piped", compute="mfma", tile="128x128")
+    torch.cuda.synchronize()
+    print("8192^3 timed variant done; oracle on the whole product", flush=True)
+    check_bound(C.cpu().numpy(), Ad.cpu().numpy(), Bd.cpu().numpy(), what="8192^3 MFMA piped S=2 (whole output)")
+
+
 @pytest.mark.parametrize("M", [3584, 4608])
 def test_residency_capped_grids(M):
     """Grids where the launch caps residency (896 tiles: piped S=3 holds 2

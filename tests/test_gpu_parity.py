@@ -234,8 +234,9 @@ def test_closed_forms_identity_and_permutation():
 
 
 def test_page_input_pattern_relative_tolerance():
-    """The day-74 program's own inputs and its relative 1e-4 check."""
-    for n in (512, 1024):
+    """The day-74 program's own inputs and its relative 1e-4 check, at the
+    program's three sizes ("pipelined_gemm.cu", main: kSizes)."""
+    for n in (512, 1024, 2048):
         A = datagen.page_pattern_a(n * n).reshape(n, n)
         B = datagen.page_pattern_b(n * n).reshape(n, n)
         ref = oracle.gemm_f64(A, B)
