@@ -61,6 +61,7 @@ def lib():
         L.mgemm_sgemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, vp]
         L.mgemm_sgemm_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci, vp]
         L.mgemm_tile_copy.argtypes = [i64, i64, vp, i64, vp, i64, ci, vp]
+        L.mgemm_plain_copy.argtypes = [i64, i64, vp, i64, vp, i64, vp]
         L.mgemm_plan_sgemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, ci, ci, ci, ci,
                                        ctypes.POINTER(Plan)]
         L.mgemm_ring_trace.argtypes = [ci, ci, ci, ci, ctypes.POINTER(ctypes.c_int), ci]
@@ -76,7 +77,7 @@ def lib():
                                           ctypes.POINTER(ctypes.c_int)]
         L.mgemm_status_string.argtypes = [ci]
         L.mgemm_status_string.restype = ctypes.c_char_p
-        for f in (L.mgemm_sgemm, L.mgemm_sgemm_ex, L.mgemm_tile_copy, L.mgemm_plan_sgemm,
+        for f in (L.mgemm_sgemm, L.mgemm_sgemm_ex, L.mgemm_tile_copy, L.mgemm_plain_copy, L.mgemm_plan_sgemm,
                   L.mgemm_ring_trace, L.mgemm_fill_trace, L.mgemm_version, L.mgemm_blocks_per_cu, L.mgemm_gemm16,
                   L.mgemm_plan_gemm16, L.mgemm_attention, L.mgemm_plan_attention):
             f.restype = ci
@@ -121,6 +122,10 @@ def mgemm_plan_attention(batch, heads, seq_q, seq_k, head_dim, Q, q_sb, q_sh, q_
 
 def mgemm_tile_copy(rows, cols, src, lds, dst, ldd, stages, stream) -> int:
     return lib().mgemm_tile_copy(rows, cols, src, lds, dst, ldd, stages, stream)
+
+
+def mgemm_plain_copy(rows, cols, src, lds, dst, ldd, stream) -> int:
+    return lib().mgemm_plain_copy(rows, cols, src, lds, dst, ldd, stream)
 
 
 def mgemm_status_string(status: int) -> str:
@@ -326,6 +331,21 @@ def tile_copy(src, dst=None, *, stages: int = 3, stream=None):
     st = mgemm_tile_copy(src.shape[0], src.shape[1], ps, lds, pd, ldd, stages, _stream(stream))
     if st != OK:
         raise MgemmError(st, "mgemm_tile_copy")
+    return dst
+
+
+def plain_copy(src, dst=None, *, stream=None):
+    """dst = src through mgemm_plain_copy (no LDS ring: the copy ceiling)."""
+    import torch
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=torch.float32, device=src.device)
+    if tuple(dst.shape) != tuple(src.shape):
+        raise ValueError("dst has the wrong shape")
+    ps, lds = _mat(src, "src")
+    pd, ldd = _mat(dst, "dst")
+    st = mgemm_plain_copy(src.shape[0], src.shape[1], ps, lds, pd, ldd, _stream(stream))
+    if st != OK:
+        raise MgemmError(st, "mgemm_plain_copy")
     return dst
 
 

@@ -68,6 +68,20 @@ struct SwzA {
     MG_HD static constexpr int f(int r) { return (r >> 2) & 3; }
 };
 
+// Rows of 128 B (the 16-bit tiles' A slices, fp32 A slices of 32 k): 16
+// consecutive rows on distinct 16-byte bank groups.
+struct SwzA16 {
+    MG_HD static constexpr int f(int r) { return (r >> 1) & 7; }
+};
+// Rows of 256 B (fp32 A slices of 64 k): 16 consecutive rows on distinct
+// 16-byte bank groups.
+struct SwzA256 {
+    MG_HD static constexpr int f(int r) { return r & 15; }
+};
+// The A-slice swizzle for a row of KPS fp32 values.
+template <int KPS>
+using SwzRowsOf = typename std::conditional<KPS == 16, SwzA, typename std::conditional<KPS == 32, SwzA16, SwzA256>::type>::type;
+
 // ROWS x COLS fp32 slice; chunk (r, c4) (4 floats) lives at chunk position
 // r * CPR + (c4 ^ f(r)).
 template <int ROWS, int COLS, class Swz>
@@ -234,13 +248,16 @@ struct ValuTile {
 // MFMA: 4 waves as 2 x 2; each wave owns WTM x WTN tiles of 32 x 32, computed
 // with v_mfma_f32_32x32x2_f32. Lane l supplies A[m0 + l%32][k_l] and
 // B[k_l][n0 + l%32] with k_l = 8kb + 4(l/32) + s in MFMA step s, so the four
-// steps of a half slice cover its eight k values.
-template <int WTM, int WTN>
+// steps of an 8-k group cover its eight k values. A K slice holds KPS_ k
+// values (16, 32 or 64): the MFMA sequence of each accumulator depends on the
+// absolute k only, not on how the slices cut it.
+template <int WTM, int WTN, int KPS_ = kBK>
 struct MfmaTile {
     static constexpr int BM = 64 * WTM, BN = 64 * WTN;
-    using LA = Layout<BM, kBK, SwzA>;
-    using LB = Layout<kBK, BN, SwzNone>;
-    static constexpr int A_STEP = kBK, B_STEP = kBK, KPS = kBK, EPW = 1, WAVES = kWaves;
+    static constexpr int A_STEP = KPS_, B_STEP = KPS_, KPS = KPS_, EPW = 1, WAVES = kWaves;
+    static_assert(KPS == 16 || KPS == 32 || KPS == 64, "K slice");
+    using LA = Layout<BM, KPS, SwzRowsOf<KPS>>;
+    using LB = Layout<KPS, BN, SwzNone>;
     f32x16 acc[WTM][WTN];
     int wm, wn, lane;
 
@@ -272,7 +289,7 @@ struct MfmaTile {
     __device__ void compute(const unsigned char *As, const unsigned char *Bs) {
         const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
-        for (int kb = 0; kb < kBK / 8; ++kb) {
+        for (int kb = 0; kb < KPS / 8; ++kb) {
             f32x4 a[WTM];
 #pragma unroll
             for (int ta = 0; ta < WTM; ++ta) {
@@ -339,9 +356,6 @@ struct MfmaTile {
 // addresses row k0 + q/4, columns nb + 4(q%4) .. +3, lane i receives
 // B[k0 .. k0+3][nb + i], so two such reads give B[16ks + 8(l/32) + 0..7][n],
 // the same k values its A operand holds.
-struct SwzA16 { // rows of 128 B: 16 consecutive rows on distinct 16-byte bank groups
-    MG_HD static constexpr int f(int r) { return (r >> 1) & 7; }
-};
 #ifndef MGEMM_SWZB16
 #define MGEMM_SWZB16 2
 #endif
@@ -591,8 +605,14 @@ struct CfgValu128 {
     using Tile = ValuTile<128, 128, 8, 8>;
     static constexpr int BM = 128, BN = 128;
 };
-struct CfgMfma64 {
-    using Tile = MfmaTile<1, 1>;
+// 64 x 64 MFMA tile with a K slice of 32 or 64: one wave per 32 x 32 tile
+// issues only 4 MFMAs per 8 k, so the slice's fixed costs (barrier, fill
+// issue, first LDS reads) are spread over more of them; the planner takes
+// 64 where each CU holds one block, 32 where several blocks share it (the
+// longer slot would cut their residency).
+template <int KPS>
+struct CfgMfma64K {
+    using Tile = MfmaTile<1, 1, KPS>;
     static constexpr int BM = 64, BN = 64;
 };
 struct CfgMfma128 {
@@ -1031,8 +1051,12 @@ __global__ void __launch_bounds__(kWsThreads) sgemm_ws_kernel(GemmArgs g) {
     using Tile = typename Cfg::Tile;
     using Ops = PipedOps<Tile, W>;
     static_assert(S >= 1 && S <= kMaxPipedStages, "stages");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[S * Ops::SLOT];
+    // a ring deeper than the CU's LDS is never planned; its kernel is empty
+    constexpr bool kFits = S * Ops::SLOT + (int)sizeof(WsCounters) <= kLdsBytes;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kFits ? S * Ops::SLOT : 1024];
     __shared__ WsCounters ctr;
+    if constexpr (!kFits)
+        return;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1115,10 +1139,8 @@ __global__ void __launch_bounds__(kThreads) zero_kernel(float *C, int M, int N, 
 // non-temporal stores). Keeping stores out of the filling waves keeps their
 // vmcnt a pure count of their own fills, so the ring's waits are exact.
 // Block b copies runs b, b + G, b + 2G, ... (G = grid size) of R consecutive
-// tiles. With R = 4 where a tile-row holds 4 tiles or more, the tiles in one
-// block's ring share memory rows (1 KB of each row per block instead of
-// 256 B from each of 8 XCDs): 5.3 -> 5.8 TB/s for a 16384-wide matrix. Where
-// tiles are whole contiguous rows (64 columns), R = 1 measured faster.
+// tiles; the launch makes G the number of runs (one run per block), so the
+// blocks in flight, dispatched in order, sweep one window of memory.
 constexpr int kCopyWaves = 8;
 constexpr int kCopyFillWaves = 4;
 constexpr int kCopyThreads = 64 * kCopyWaves;
@@ -1224,6 +1246,35 @@ __global__ void __launch_bounds__(kCopyThreads) tile_copy_kernel(CopyArgs a) {
     const int nruns = (a.ntiles + (1 << a.run_log2) - 1) >> a.run_log2;
     const int T = ((nruns - (int)blockIdx.x + ops.G - 1) / ops.G) << a.run_log2;
     piped_schedule<S>(T, ops);
+}
+
+// ---- plain copy (the ceiling the tile copy is read against) -------------------------
+//
+// dst = src with no LDS and no ring: each lane moves one 16-byte chunk (or
+// one 4-byte element where alignment forbids 16) with a non-temporal load
+// into a register and a non-temporal store, and the grid holds one lane per
+// chunk, dispatched in order. It is the practical HBM copy rate of the
+// device, measured the same way as the tile copy.
+constexpr int kPlainThreads = 256;
+
+struct PlainCopyArgs {
+    const float *src;
+    float *dst;
+    long long lds, ldd, rows, cpr; // cpr: units (chunks or elements) per row
+};
+
+template <int W>
+__global__ void __launch_bounds__(kPlainThreads) plain_copy_kernel(PlainCopyArgs a) {
+    const long long u = (long long)blockIdx.x * kPlainThreads + threadIdx.x;
+    if (u >= a.rows * a.cpr)
+        return;
+    const long long r = u / a.cpr, c = u - r * a.cpr;
+    if constexpr (W == 16) {
+        const f32x4 v = __builtin_nontemporal_load((const f32x4 *)(a.src + r * a.lds) + c);
+        __builtin_nontemporal_store(v, (f32x4 *)(a.dst + r * a.ldd) + c);
+    } else {
+        __builtin_nontemporal_store(__builtin_nontemporal_load(a.src + r * a.lds + c), a.dst + r * a.ldd + c);
+    }
 }
 
 } // namespace mgemm

@@ -28,6 +28,7 @@ namespace {
 constexpr int64_t kMaxLd = int64_t(1) << 21;     // 256 rows x 2^21 words x 4 B: in-block byte offsets stay below 2^31
 constexpr int64_t kMaxExtent = int64_t(1) << 31; // rows * ld per operand, in elements
 constexpr int kMaxStages16 = 4;                  // asynchronous ring depth of the 16-bit GEMM
+constexpr int64_t kCUs = 256;                    // MI355X compute units, for the planner's wave model
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -128,24 +129,33 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
     }
     const int bm = tile == MGEMM_TILE_256x128 ? 256 : tile == MGEMM_TILE_128x128 ? 128 : 64;
     const int bn = tile == MGEMM_TILE_64x64 ? 64 : 128;
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    // the 64x64 MFMA tile's K slice, from the shape alone (so that every
+    // fill and depth of one shape runs the same MFMA sequence): 64 k where
+    // each of the 256 CUs gets one block at most, else 32 (measured,
+    // piped, TFLOP/s: 16384x64x4096 16/32/64 k: 79/97/106; 4099x3001x1537:
+    // 117/117/111)
+    const int bk = (compute == MGEMM_COMPUTE_MFMA && tile == MGEMM_TILE_64x64) ? (tiles <= kCUs ? 64 : 32) : kBK;
     mgemm_plan_t p;
     std::memset(&p, 0, sizeof p);
     p.compute = compute;
     p.tile = tile;
     p.bm = bm;
     p.bn = bn;
-    p.bk = kBK;
+    p.bk = bk;
     p.threads = fill == MGEMM_FILL_PIPED_WS ? kWsThreads : kThreads;
     p.blocks = (int)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
     p.load_bytes = W;
-    p.slices = (int)((K + kBK - 1) / kBK);
+    p.slices = (int)((K + bk - 1) / bk);
     p.stages = stages;
     p.fill_mode = fill;
-    p.lds_bytes = stages * (bm * kBK + kBK * bn) * 4 + (fill == MGEMM_FILL_PIPED_WS ? (int)sizeof(WsCounters) : 0);
+    p.lds_bytes = stages * (bm * bk + bk * bn) * 4 + (fill == MGEMM_FILL_PIPED_WS ? (int)sizeof(WsCounters) : 0);
     // one 64-lane instruction moves 64*W bytes; a slice of both operands is
-    // (bm+bn)*16*4 bytes, shared by the 4 waves
-    p.loads_per_slice = ((bm + bn) * kBK * 4) / (64 * W) / kWaves;
+    // (bm+bn)*bk*4 bytes, shared by the 4 waves
+    p.loads_per_slice = ((bm + bn) * bk * 4) / (64 * W) / kWaves;
     p.max_vmcnt = fill != MGEMM_FILL_SYNC ? std::min(63, std::max(0, stages - 2) * p.loads_per_slice) : 0;
+    if (p.lds_bytes > kLdsBytes) // a ring deeper than the CU's LDS
+        return MGEMM_ERR_UNSUPPORTED;
     if (pl)
         *pl = p;
     return MGEMM_OK;
@@ -191,7 +201,8 @@ int current_device(int *dev) {
     MG_GEMM_SYNC_INST(CFG, 1, 4) MG_GEMM_SYNC_INST(CFG, 2, 4) MG_GEMM_SYNC_INST(CFG, 3, 4)
 MG_GEMM_CFG(CfgValu64)
 MG_GEMM_CFG(CfgValu128)
-MG_GEMM_CFG(CfgMfma64)
+MG_GEMM_CFG(CfgMfma64K<32>)
+MG_GEMM_CFG(CfgMfma64K<64>)
 MG_GEMM_CFG(CfgMfma128)
 MG_GEMM_CFG(CfgMfma256x128)
 #define MG_GEMM16_INST(CFG, S, W)                                                                        \
@@ -213,6 +224,8 @@ MG_GEMM16_CFG(CfgH256x256<false>)
     template __global__ void mgemm::tile_copy_kernel<S, 16, false>(mgemm::CopyArgs);                     \
     template __global__ void mgemm::tile_copy_kernel<S, 4, true>(mgemm::CopyArgs);                       \
     template __global__ void mgemm::tile_copy_kernel<S, 4, false>(mgemm::CopyArgs);
+template __global__ void mgemm::plain_copy_kernel<16>(mgemm::PlainCopyArgs);
+template __global__ void mgemm::plain_copy_kernel<4>(mgemm::PlainCopyArgs);
 MG_COPY_INST(1)
 MG_COPY_INST(2)
 MG_COPY_INST(3)
@@ -283,8 +296,10 @@ const void *select_gemm(const mgemm_plan_t &p) {
                                             : gemm_kernel<CfgValu64>(p.stages, piped, p.load_bytes);
     if (p.tile == MGEMM_TILE_256x128)
         return gemm_kernel<CfgMfma256x128>(p.stages, piped, p.load_bytes);
-    return p.tile == MGEMM_TILE_128x128 ? gemm_kernel<CfgMfma128>(p.stages, piped, p.load_bytes)
-                                        : gemm_kernel<CfgMfma64>(p.stages, piped, p.load_bytes);
+    if (p.tile == MGEMM_TILE_128x128)
+        return gemm_kernel<CfgMfma128>(p.stages, piped, p.load_bytes);
+    return p.bk == 64 ? gemm_kernel<CfgMfma64K<64>>(p.stages, piped, p.load_bytes)
+                      : gemm_kernel<CfgMfma64K<32>>(p.stages, piped, p.load_bytes);
 }
 
 int launch(const void *fn, int blocks, void *arg, hipStream_t stream, int threads = kThreads, int dyn_lds = 0) {
@@ -700,7 +715,7 @@ bool fill_trace_kind(int kind, FillRecorder &rec) {
     switch (kind) {
     case 0: trace_gemm_fill<CfgValu64, W, PIPED>(rec); return true;
     case 1: trace_gemm_fill<CfgValu128, W, PIPED>(rec); return true;
-    case 2: trace_gemm_fill<CfgMfma64, W, PIPED>(rec); return true;
+    case 2: trace_gemm_fill<CfgMfma64K<32>, W, PIPED>(rec); return true;
     case 3: trace_gemm_fill<CfgMfma128, W, PIPED>(rec); return true;
     case 4: trace_gemm_fill<CfgMfma256x128, W, PIPED>(rec); return true;
     case 5: trace_gemm_fill<CfgH128<true>, W, PIPED>(rec); return true;
@@ -713,6 +728,7 @@ bool fill_trace_kind(int kind, FillRecorder &rec) {
             return false;
         trace_copy_fill<W>(rec);
         return true;
+    case 11: trace_gemm_fill<CfgMfma64K<64>, W, PIPED>(rec); return true;
     default: return false;
     }
 }
@@ -860,21 +876,44 @@ int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, f
     if (ntiles > kMaxExtent - 4) // tile ids of a final partial run stay below 2^31
         return MGEMM_ERR_UNSUPPORTED;
     a.ntiles = (int)ntiles;
-    a.run_log2 = a.tcols >= 4 ? 2 : 0;
+    // One block per run of 2 adjacent tiles (1 tile without a ring to
+    // pipeline through), the whole grid in one launch: blocks are dispatched
+    // in order as others retire, so the blocks in flight cover one sliding
+    // window of memory. Measured on the 1 GiB copy, S=3 (TB/s, 16384-wide /
+    // 64-wide views): this grid 6.10 / 6.09; a persistent grid taking every
+    // G-th run of 4 (resp. 1) tiles 5.78 / 5.89; runs of 4 in this grid
+    // 5.98 / 5.87.
+    a.run_log2 = stages >= 2 ? 1 : 0;
     const void *fn = copy_kernel(stages, W, vst);
-    // persistent grid: as many blocks as fit on the device at once
-    static std::atomic<int> occ_cache[kMaxPipedStages][2][2];
-    std::atomic<int> &oc = occ_cache[stages - 1][W == 16][vst];
-    int occ = oc.load(std::memory_order_relaxed);
-    if (occ == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kCopyThreads, 0) != hipSuccess || occ < 1)
-            occ = 1;
-        oc.store(occ, std::memory_order_relaxed);
-    }
-    const int64_t resident = (int64_t)occ * g_cus[dev].load(std::memory_order_relaxed);
-    const int blocks = (int)std::min<int64_t>(ntiles, resident > 0 ? resident : 256);
+    const int64_t runs = (ntiles + (1 << a.run_log2) - 1) >> a.run_log2;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    return launch(fn, blocks, &a, s, kCopyThreads);
+    return launch(fn, (int)runs, &a, s, kCopyThreads);
+}
+
+int mgemm_plain_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, float *dst, int64_t ldd,
+                     void *stream) {
+    int st;
+    if ((st = check_matrix(src, rows, cols, lds)) != MGEMM_OK || (st = check_matrix(dst, rows, cols, ldd)) != MGEMM_OK)
+        return st;
+    if (overlap(span(src, rows, cols, lds), span(dst, rows, cols, ldd)))
+        return MGEMM_ERR_ALIAS;
+    if (rows == 0 || cols == 0)
+        return MGEMM_OK;
+    int dev;
+    if ((st = current_device(&dev)) != MGEMM_OK)
+        return st;
+    const bool w16 = aligned16(src) && aligned16(dst) && lds % 4 == 0 && ldd % 4 == 0 && cols % 4 == 0;
+    PlainCopyArgs a;
+    a.src = src;
+    a.dst = dst;
+    a.lds = lds;
+    a.ldd = ldd;
+    a.rows = rows;
+    a.cpr = w16 ? cols / 4 : cols;
+    const int64_t units = rows * a.cpr;
+    const int64_t blocks = (units + kPlainThreads - 1) / kPlainThreads;
+    return launch(w16 ? (const void *)&plain_copy_kernel<16> : (const void *)&plain_copy_kernel<4>, (int)blocks, &a,
+                  reinterpret_cast<hipStream_t>(stream), kPlainThreads);
 }
 
 int mgemm_blocks_per_cu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,

@@ -87,17 +87,18 @@ def parse():
     p.add_argument("--oracle-full", action="store_true",
                    help="also time the oracle once on the whole problem (all rows; about 20 s on 16 host cores)")
     p.add_argument("--profile", action="store_true",
-                   help="only run a few launches of the timed GEMM, the 1 GiB tile copy (3 stages), a plain "
-                        "1 GiB device copy (the calibration kernel for hardware byte counters), the 16-bit GEMM "
+                   help="only run a few launches of the timed GEMM, the 1 GiB tile copy (3 stages), the plain "
+                        "1 GiB copy (the calibration kernel for hardware byte counters), the 16-bit GEMM "
                         "and the attention kernel, for rocprofv3")
     return p.parse_args()
 
 
 def profile_mode(args):
     """Launches for counter collection, `steps` of each, no timing: the timed
-    GEMM, its VALU twin, the 1 GiB tile copy in both array views, a plain
-    1 GiB device copy (the calibration kernel for hardware byte counters),
-    the 16-bit GEMM and the attention kernel in their default plans."""
+    GEMM, its VALU twin, the 1 GiB tile copy in both array views, the plain
+    1 GiB copy (mgemm_plain_copy, the calibration kernel for hardware byte
+    counters), the 16-bit GEMM and the attention kernel in their default
+    plans."""
     import torch
 
     import async_global_shared_amd as m
@@ -120,9 +121,10 @@ def profile_mode(args):
         torch.cuda.synchronize()
         print(f"profile: {args.steps} x tile_copy 1 GiB as {shape[0]}x{shape[1]} S=3", flush=True)
     for _ in range(args.steps):
-        dst.copy_(src)
+        m.plain_copy(src.view(*COPY_VIEWS[0]), dst.view(*COPY_VIEWS[0]))
     torch.cuda.synchronize()
-    print(f"profile: {args.steps} x plain device copy 1 GiB (calibration: 2^30 B read, 2^30 B written)", flush=True)
+    print(f"profile: {args.steps} x plain copy 1 GiB (the copy ceiling and the counters' calibration: "
+          f"2^30 B read, 2^30 B written)", flush=True)
     del src, dst
     A16 = datagen.grid16_torch(datagen.SEED_A, n, n, "bf16", device="cuda")
     B16 = datagen.grid16_torch(datagen.SEED_B, n, n, "bf16", device="cuda")
@@ -376,15 +378,26 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8, with_oracle=True):
     dst = torch.empty_like(src)
     nbytes = 2.0 * n_el * 4
     copy = {}
+    t = timed_launches(lambda: m.plain_copy(src.view(*COPY_VIEWS[0]), dst.view(*COPY_VIEWS[0])), repeats=REPEATS)
+    if not torch.equal(src, dst):
+        raise SystemExit("plain copy changed bytes")
+    ceiling = nbytes / (t["ms_median"] * 1e-3) / 1e9
+    copy["plain_copy_ceiling"] = {"ms": round(t["ms_median"], 4), "ms_min": round(t["ms_min"], 4),
+                                  "GBps": round(ceiling, 1), "pct_hbm_peak": round(100 * ceiling / PEAK_HBM_GBS, 2),
+                                  "what": "mgemm_plain_copy: no LDS ring, one 16-byte lane per chunk, non-temporal"}
     for shape in COPY_VIEWS:
         view = f"{shape[0]}x{shape[1]}"
         for S in (1, 2, 3):
+            dst.fill_(float("nan"))
+            m.tile_copy(src.view(*shape), dst.view(*shape), stages=S)
+            torch.cuda.synchronize()
+            if not torch.equal(src, dst):
+                raise SystemExit(f"tile copy changed bytes ({view} S={S})")
             t = timed_launches(lambda: m.tile_copy(src.view(*shape), dst.view(*shape), stages=S), repeats=REPEATS)
             gbs = nbytes / (t["ms_median"] * 1e-3) / 1e9
             copy[f"{view}_S{S}"] = {"ms": round(t["ms_median"], 4), "ms_min": round(t["ms_min"], 4), "GBps": round(gbs, 1),
-                                    "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
-        if not torch.equal(src, dst):
-            raise SystemExit("tile copy changed bytes")
+                                    "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                                    "frac_of_plain_copy": round(gbs / ceiling, 3)}
     t = timed_launches(lambda: dst.copy_(src), repeats=REPEATS)
     copy["torch_copy_context"] = {"ms": round(t["ms_median"], 4),
                                   "GBps": round(nbytes / (t["ms_median"] * 1e-3) / 1e9, 1)}

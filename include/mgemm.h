@@ -57,9 +57,11 @@ struct mgemm_plan; /* defined below (mgemm_plan_t) */
 #define MGEMM_COMPUTE_VALU 0 /* per element fma chain, k ascending (the pages' computeTile) */
 #define MGEMM_COMPUTE_MFMA 1 /* v_mfma_f32_32x32x2_f32 wave tiles */
 
-/* tile: block tile of C (BM x BN, K slice 16, 256 threads). */
+/* tile: block tile of C (BM x BN, K slice 16 unless noted, 256 threads). */
 #define MGEMM_TILE_AUTO 0      /* 64x64 or 128x128, whichever a wave model of the CUs estimates faster */
-#define MGEMM_TILE_64x64 1   /* VALU: 4x4 micro-tile per thread (the pages' shape) */
+#define MGEMM_TILE_64x64 1   /* VALU: 4x4 micro-tile per thread (the pages' shape); MFMA: one 32x32
+                                tile per wave, K slice 64 where the grid gives each of 256 CUs one
+                                block at most, else 32 (chosen from the shape alone) */
 #define MGEMM_TILE_128x128 2 /* VALU: 8x8 micro-tile; MFMA: 2x2 32x32 tiles per wave */
 #define MGEMM_TILE_256x128 3 /* MFMA only: 4x2 32x32 tiles per wave (BM 256, BN 128) */
 #define MGEMM_TILE_256x256 4 /* 16-bit only: 8 waves of 4x2 32x32 tiles (BM 256, BN 256) */
@@ -192,6 +194,18 @@ int mgemm_plan_attention(int64_t batch, int64_t heads, int64_t seq_q, int64_t se
 int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds,
                     float *dst, int64_t ldd, int stages, void *stream);
 
+/*
+ * dst[0:rows, 0:cols] = src[0:rows, 0:cols] with no LDS and no ring: each
+ * lane moves one 16-byte chunk (4-byte element where bases, ld or cols
+ * forbid 16) through a register, with non-temporal loads and stores, over a
+ * grid of one lane per chunk. This is the practical HBM copy rate of the
+ * device, the ceiling the tile copy's fill bandwidth is read against. It is
+ * not a row of the method itself. Validation and ownership as
+ * mgemm_tile_copy.
+ */
+int mgemm_plain_copy(int64_t rows, int64_t cols, const float *src, int64_t lds,
+                     float *dst, int64_t ldd, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *mgemm_status_string(int status);
 
@@ -272,9 +286,10 @@ int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *event
  * filling-wave rules the kernels instantiate (the tile loader and zero-fill
  * row of the method: coalesced 16-byte or 4-byte lanes, each lane's
  * destination in the LDS slot). kind: 0 fp32 VALU 64x64, 1 VALU 128x128,
- * 2 fp32 MFMA 64x64, 3 MFMA 128x128, 4 MFMA 256x128, 5 16-bit 128x128,
- * 6 16-bit 256x128, 7 16-bit 256x256, 8 attention head dim 64, 9 head dim
- * 128, 10 tile copy (MGEMM_FILL_PIPED only); load_bytes 16 or 4;
+ * 2 fp32 MFMA 64x64 with a 32-k slice, 3 MFMA 128x128, 4 MFMA 256x128,
+ * 5 16-bit 128x128, 6 16-bit 256x128, 7 16-bit 256x256, 8 attention head
+ * dim 64, 9 head dim 128, 10 tile copy (MGEMM_FILL_PIPED only), 11 fp32
+ * MFMA 64x64 with a 64-k slice; load_bytes 16 or 4;
  * fill_mode MGEMM_FILL_SYNC (register-staged) or MGEMM_FILL_PIPED.
  * Events are 6 ints written to events[0 .. 6*cap). The first is a header
  * {-1, slot bytes, rows and 32-bit columns of operand 0, rows and columns of

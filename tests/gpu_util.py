@@ -39,6 +39,17 @@ def out_device(M: int, N: int, ldc: int | None = None, offset: int = 0) -> torch
     return buf[offset:offset + M * ldc].view(M, ldc)[:, :N]
 
 
+def ring_fits(M, N, K, **kw) -> bool:
+    """Whether the library plans this launch; the only refusal expected of a
+    valid call is a ring deeper than the CU's LDS (MGEMM_ERR_UNSUPPORTED)."""
+    try:
+        m.plan(M, N, K, **kw)
+        return True
+    except m.MgemmError as e:
+        assert e.status == m.ERR_UNSUPPORTED, (M, N, K, kw, e.status)
+        return False
+
+
 def run(Ad, Bd, Cd, *, compute, tile, fill, stages, loader="auto"):
     m.sgemm(Ad, Bd, Cd, stages=stages, fill=fill, compute=compute, tile=tile, loader=loader)
     torch.cuda.synchronize()

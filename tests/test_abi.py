@@ -92,6 +92,17 @@ def test_copy_validation():
     assert f(0, 10, 0, 10, 0, 10, 2, None) == m.OK
 
 
+def test_plain_copy_validation():
+    f = m.mgemm_plain_copy
+    assert f(10, 10, A0, 9, B0, 10, None) == m.ERR_ARG
+    assert f(10, 10, A0, 10, B0, 9, None) == m.ERR_ARG
+    assert f(10, 10, A0, 10, A0 + 40, 10, None) == m.ERR_ALIAS
+    assert f(10, 10, 0, 10, B0, 10, None) == m.ERR_ARG
+    assert f(-1, 10, A0, 10, B0, 10, None) == m.ERR_ARG
+    assert f(0, 10, 0, 10, 0, 10, None) == m.OK
+    assert f(1 << 20, 4096, A0, 4096, B0, 4096, None) == m.ERR_UNSUPPORTED
+
+
 def test_plan_tiles_loaders_and_lds():
     p = m.plan(256, 256, 256)
     assert (p["bm"], p["bn"], p["bk"], p["threads"], p["blocks"]) == (64, 64, 16, 256, 16)
@@ -320,9 +331,9 @@ def test_split_ring_schedule(S):
         simulate_piped([e for e in ev if e[:2] != (7, 2)], S, 4, split=True)
 
 
-FILL_KINDS = {0: "fp32 VALU 64", 1: "fp32 VALU 128", 2: "fp32 MFMA 64", 3: "fp32 MFMA 128", 4: "fp32 MFMA 256x128",
-              5: "16-bit 128", 6: "16-bit 256x128", 7: "16-bit 256x256", 8: "attention D64", 9: "attention D128",
-              10: "tile copy"}
+FILL_KINDS = {0: "fp32 VALU 64", 1: "fp32 VALU 128", 2: "fp32 MFMA 64 (32-k slice)", 3: "fp32 MFMA 128",
+              4: "fp32 MFMA 256x128", 5: "16-bit 128", 6: "16-bit 256x128", 7: "16-bit 256x256", 8: "attention D64",
+              9: "attention D128", 10: "tile copy", 11: "fp32 MFMA 64 (64-k slice)"}
 
 
 @pytest.mark.parametrize("kind", sorted(FILL_KINDS))
@@ -423,8 +434,16 @@ def _kernels(isa):
     return out
 
 
+def _mangled(cfg):
+    """Itanium-mangled config name: "CfgX" or "CfgX<n>" (an int template)."""
+    mm = re.fullmatch(r"(\w+)<(\d+)>", cfg)
+    if mm:
+        return f"{len(mm[1])}{mm[1]}ILi{mm[2]}EE"
+    return f"{len(cfg)}{cfg}"
+
+
 def _name(cfg, S, piped, W):
-    return f"_ZN5mgemm12sgemm_kernelINS_{len(cfg)}{cfg}ELi{S}ELb{int(piped)}ELi{W}EEEvNS_8GemmArgsE"
+    return f"_ZN5mgemm12sgemm_kernelINS_{_mangled(cfg)}ELi{S}ELb{int(piped)}ELi{W}EEEvNS_8GemmArgsE"
 
 
 @pytest.fixture(scope="module")
@@ -434,7 +453,35 @@ def isa():
     return _kernels(open(m.ISA_PATH).read())
 
 
-CFGS = ["CfgValu64", "CfgValu128", "CfgMfma64", "CfgMfma128", "CfgMfma256x128"]
+CFGS = ["CfgValu64", "CfgValu128", "CfgMfma64K<32>", "CfgMfma64K<64>", "CfgMfma128", "CfgMfma256x128"]
+# a problem each config is planned for: (M, N, K, tile, compute)
+CFG_PLAN = {"CfgValu64": (1024, 1024, 1024, "64x64", "valu"), "CfgValu128": (1024, 1024, 1024, "128x128", "valu"),
+            "CfgMfma64K<32>": (2048, 2048, 1024, "64x64", "mfma"), "CfgMfma64K<64>": (1024, 1024, 1024, "64x64", "mfma"),
+            "CfgMfma128": (1024, 1024, 1024, "128x128", "mfma"), "CfgMfma256x128": (1024, 1024, 1024, "256x128", "mfma")}
+
+
+def _cfg_plan(cfg, S, fill="piped", W=16):
+    """The plan of cfg's problem at depth S, or None where the ring exceeds the LDS."""
+    M, N, K, tile, compute = CFG_PLAN[cfg]
+    try:
+        p = m.plan(M, N, K, stages=S, fill=fill, tile=tile, compute=compute, loader="b128" if W == 16 else "b32")
+    except m.MgemmError as e:
+        assert e.status == m.ERR_UNSUPPORTED
+        return None
+    assert p["bk"] == (int(cfg[-3:-1]) if "<" in cfg else 16)
+    return p
+
+
+def test_every_config_and_depth_that_fits_is_planned():
+    """Rings within the 160 KiB of LDS are planned; deeper ones are refused
+    (their kernels are empty) rather than run."""
+    for cfg in CFGS:
+        for S in range(1, 7):
+            p = _cfg_plan(cfg, S)
+            slot = (CFG_PLAN[cfg][3], int(cfg[-3:-1]) if "<" in cfg else 16)
+            bm, bn = (int(x) for x in slot[0].split("x"))
+            fits = S * (bm + bn) * slot[1] * 4 <= 160 * 1024
+            assert (p is not None) == fits, (cfg, S)
 
 
 @pytest.mark.parametrize("cfg", CFGS)
@@ -443,6 +490,8 @@ def test_isa_fill_instructions(isa, cfg):
     kernels fill through VGPRs (ds_write) and have no LDS-direct load."""
     for S in range(1, 7):
         for W in (16, 4):
+            if _cfg_plan(cfg, S) is None:
+                continue
             body = "\n".join(isa[_name(cfg, S, True, W)])
             width = "dwordx4" if W == 16 else "dword"
             assert re.search(rf"buffer_load_{width} .* lds", body), (cfg, S, W)
@@ -533,16 +582,16 @@ def test_isa_compute_does_not_drain_the_prefetch(isa, cfg):
     op = "v_mfma_f32_32x32x2_f32" if "Mfma" in cfg else "v_fmac_f32"
     for S in range(2, 7):
         for W in (16, 4):
+            p = _cfg_plan(cfg, S, W=W)
+            if p is None:
+                continue
             lines = isa[_name(cfg, S, True, W)]
             drained, reached = _drain_before_compute(lines, op)
             assert reached, (cfg, S, W)
             assert not drained, (cfg, S, W)
             if S >= 3:
                 body = "\n".join(lines)
-                tile = {"CfgMfma256x128": "256x128"}.get(cfg, "128x128" if "128" in cfg else "64x64")
-                n = m.plan(1024, 1024, 1024, stages=S, tile=tile, compute="mfma" if "Mfma" in cfg else "valu",
-                           loader="b128" if W == 16 else "b32")["max_vmcnt"]
-                assert f"s_waitcnt vmcnt({n})" in body, (cfg, S, W, n)
+                assert f"s_waitcnt vmcnt({p['max_vmcnt']})" in body, (cfg, S, W, p["max_vmcnt"])
 
 
 def test_isa_drain_checker_sees_a_drain():
@@ -563,7 +612,9 @@ def test_isa_warp_specialised(isa, cfg):
     asynchronous fill."""
     for S in range(1, 7):
         for W in (16, 4):
-            name = f"_ZN5mgemm15sgemm_ws_kernelINS_{len(cfg)}{cfg}ELi{S}ELi{W}EEEvNS_8GemmArgsE"
+            if _cfg_plan(cfg, S, fill="piped_ws") is None:
+                continue
+            name = f"_ZN5mgemm15sgemm_ws_kernelINS_{_mangled(cfg)}ELi{S}ELi{W}EEEvNS_8GemmArgsE"
             body = "\n".join(isa[name])
             assert body.count("s_barrier") == 1, (cfg, S, W)
             assert "ds_add_u32" in body and "s_sleep" in body

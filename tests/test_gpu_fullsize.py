@@ -157,11 +157,18 @@ def test_sentinel_full_size_8192():
             assert bool(torch.all(C == want)), (compute, fill, S)
 
 
-@pytest.mark.parametrize("S", [2, 3])
-def test_copy_one_gib(S):
-    rows = cols = 16384  # 2^28 fp32 = 1 GiB
-    src = datagen.normal01_torch(datagen.SEED_COPY, rows * cols, device="cuda").view(rows, cols)
+@pytest.mark.parametrize("S", [1, 2, 3])
+@pytest.mark.parametrize("shape", [(16384, 16384), (4194304, 64)], ids=["16384x16384", "4194304x64"])
+def test_copy_one_gib(S, shape):
+    """The 1 GiB copy in both views the benchmark times (2^28 fp32), every
+    byte compared; then the plain copy, its ceiling."""
+    src = datagen.normal01_torch(datagen.SEED_COPY, 1 << 28, device="cuda").view(*shape)
     dst = torch.full_like(src, float("nan"))
     m.tile_copy(src, dst, stages=S)
     torch.cuda.synchronize()
     assert torch.equal(dst.view(torch.int32), src.view(torch.int32))
+    if S == 1:
+        dst.fill_(float("nan"))
+        m.plain_copy(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(dst.view(torch.int32), src.view(torch.int32))

@@ -14,7 +14,7 @@ import torch
 import async_global_shared_amd as m
 import datagen
 import oracle
-from tests.gpu_util import (FILLS, SENTINEL, STAGES, TILES, check_bound, full_rows, out_device, padded_device, run,
+from tests.gpu_util import (ring_fits, FILLS, SENTINEL, STAGES, TILES, check_bound, full_rows, out_device, padded_device, run,
                             same_bits)
 
 pytestmark = pytest.mark.gpu
@@ -67,6 +67,8 @@ LAYOUTS = {
     "padded_ld": (300, 260, 200, 204, 268, 264, (0, 0, 0)),
     "misaligned": (301, 259, 203, 207, 263, 267, (1, 3, 2)),
     "tiny_k": (130, 70, 5, 9, 70, 75, (0, 0, 0)),
+    # more than 256 64x64 tiles: the MFMA 64x64 tile's 32-k slice (fewer: 64-k)
+    "many_tiles": (1090, 1030, 83, 87, 1030, 1034, (0, 0, 0)),
 }
 
 
@@ -107,6 +109,10 @@ def test_deep_piped_rings(layout):
                             stages=1))
         check_bound(ref[:, :N], A, B, what=f"{layout} {compute} {tile} sync S=1")
         for S in (4, 5, 6):
+            if not ring_fits(M, N, K, stages=S, fill="piped", compute=compute, tile=tile, lda=K + 3, ldb=ldb, ldc=ldc):
+                with pytest.raises(m.MgemmError):  # refused, never run on a ring the LDS cannot hold
+                    run(Ad, Bd, out_device(M, N, ldc, offset=oc), compute=compute, tile=tile, fill="piped", stages=S)
+                continue
             for ld in ("auto", "b32"):
                 C = full_rows(run(Ad, Bd, out_device(M, N, ldc, offset=oc), compute=compute, tile=tile,
                                   fill="piped", stages=S, loader=ld))
@@ -126,6 +132,8 @@ def test_warp_specialised_ring(layout):
                             stages=1))
         check_bound(ref[:, :N], A, B, what=f"{layout} {compute} {tile} sync S=1")
         for S in range(1, 7):
+            if not ring_fits(M, N, K, stages=S, fill="piped_ws", compute=compute, tile=tile, lda=lda, ldb=ldb, ldc=ldc):
+                continue
             for ld in ("auto", "b32"):
                 C = full_rows(run(Ad, Bd, out_device(M, N, ldc, offset=oc), compute=compute, tile=tile,
                                   fill="piped_ws", stages=S, loader=ld))

@@ -134,3 +134,24 @@ def test_tile_copy_random(case):
         full = full_rows(dst)
         assert same_bits(np.ascontiguousarray(full[:, :cols]), want), (case, rows, cols, S)
         assert np.all(full[:, cols:] == SENTINEL), (case, rows, cols, S)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_plain_copy_random(case):
+    """The plain copy (the tile copy's ceiling) moves the same bytes, on
+    aligned (16-byte lanes) and misaligned (4-byte lanes) layouts, and
+    leaves dst's padding alone."""
+    rng = _rng(700 + case)
+    rows, cols = (int(x) for x in rng.integers(1, 900, size=2))
+    if case % 2 == 0:
+        cols = 4 * ((cols + 3) // 4)
+    ps, pd = (int(x) for x in rng.integers(0, 9, size=2)) if case % 2 else (4 * (case % 3), 8)
+    os_, od = (int(x) for x in rng.integers(0, 4, size=2)) if case % 2 else (0, 0)
+    x = datagen.matrix("normal", 800 + case, rows, cols)
+    src = padded_device(x, cols + ps, offset=os_)
+    dst = out_device(rows, cols, cols + pd, offset=od)
+    m.plain_copy(src, dst)
+    torch.cuda.synchronize()
+    full = full_rows(dst)
+    assert same_bits(np.ascontiguousarray(full[:, :cols]), oracle.copy_f32(x)), (case, rows, cols)
+    assert np.all(full[:, cols:] == SENTINEL), (case, rows, cols)
