@@ -95,7 +95,8 @@ def parse():
 
 def profile_mode(args):
     """Launches for counter collection, `steps` of each, no timing: the timed
-    GEMM, its VALU twin, the 1 GiB tile copy in both array views, the plain
+    GEMM, its VALU twin, the ragged and tall-skinny GEMMs (MFMA, piped S=2),
+    the 1 GiB tile copy in both array views, the plain
     1 GiB copy (mgemm_plain_copy, the calibration kernel for hardware byte
     counters), the 16-bit GEMM and the attention kernel in their default
     plans."""
@@ -113,6 +114,16 @@ def profile_mode(args):
         torch.cuda.synchronize()
         print(f"profile: {args.steps} x sgemm {n}^3 {compute} piped S={args.stages}", flush=True)
     del Ad, Bd, Cd
+    for name, M, N, K in CONFIG5:
+        A = datagen.uniform_pm1_torch(datagen.SEED_A, M * K, device="cuda").view(M, K)
+        B = datagen.uniform_pm1_torch(datagen.SEED_B, K * N, device="cuda").view(K, N)
+        C = torch.empty((M, N), device="cuda")
+        for _ in range(args.steps):
+            m.sgemm(A, B, C, stages=2, fill="piped", compute="mfma")
+        torch.cuda.synchronize()
+        print(f"profile: {args.steps} x sgemm {name} mfma piped S=2, plan {m.plan(M, N, K, compute='mfma')}",
+              flush=True)
+        del A, B, C
     src = datagen.normal01_torch(datagen.SEED_COPY, 1 << 28, device="cuda")
     dst = torch.empty_like(src)
     for shape in COPY_VIEWS:
