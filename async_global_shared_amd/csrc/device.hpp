@@ -450,6 +450,21 @@ struct Mfma16Tile {
                          : "=&v"(f.b[tb][0]), "=&v"(f.b[tb][1])
                          : "v"(ab[tb]), "i"(B0), "i"(B1));
     }
+    // Read R of one k step alone: R < WTM is A row tile R, the rest are the
+    // B pieces (column tile (R - WTM) / 2, row quad (R - WTM) % 2).
+    template <int KS, int R>
+    __device__ static void issue_read(unsigned aa, const unsigned *ab, Frag &f) {
+        constexpr int TA = 32 * LA::CPR * 16;
+        constexpr int B0 = (16 * KS) * LB::CPR * 16, B1 = (16 * KS + 4) * LB::CPR * 16;
+        if constexpr (R < WTM) {
+            asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f.a[R]) : "v"(aa), "i"(R * TA));
+        } else {
+            constexpr int q = R - WTM, tb = q / 2;
+            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                         : "=v"(f.b[tb][q % 2])
+                         : "v"(ab[tb]), "i"(q % 2 ? B1 : B0));
+        }
+    }
     // Wait for every LDS read of this wave; the fragment's registers are
     // outputs of the wait, so nothing reads them before it.
     __device__ static void wait_reads(Frag &f) {
@@ -505,6 +520,13 @@ struct Mfma16Tile {
     // slices); compute runs the three in a row.
     static constexpr int NKS = KPS / 16;
     static_assert(NKS % 2 == 0, "the last k step's fragment set differs from the first's");
+    // Within a k step of the body, the next step's LDS reads go one after
+    // each MFMA rather than as one burst before them, so they issue while the
+    // matrix pipe is busy (measured +1-2 % on the 256-row tiles). Only where
+    // the MFMAs outnumber the reads: the 128 x 128 tile's 4 MFMAs and 6 reads
+    // were measured 1-3 % slower this way.
+    static constexpr int NR = WTM + 2 * WTN, NM = WTM * WTN;
+    static constexpr bool kInterleave = NM >= NR;
     Frag fr[2];
     __device__ void head(const unsigned char *As, const unsigned char *Bs) {
         static_assert((WTN == 2 && (WTM == 2 || WTM == 4)) || (WTN == 4 && WTM == 4), "wait_reads covers these wave tiles");
@@ -522,10 +544,23 @@ struct Mfma16Tile {
         wait_reads(fr[0]);
         static_for<0, NKS - 1>([&](auto ksc) {
             constexpr int ks = decltype(ksc)::value;
-            issue_reads<ks + 1>(as + LA::pos(m, 2 * (ks + 1) + h) * 16, ab, fr[(ks + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma(fr[ks & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+            const unsigned aa = as + LA::pos(m, 2 * (ks + 1) + h) * 16;
+            if constexpr (kInterleave) {
+                static_for<0, NM>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    if constexpr (j < NR) {
+                        issue_read<ks + 1, j>(aa, ab, fr[(ks + 1) & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    mfma_one<j / WTN, j % WTN>(fr[ks & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            } else {
+                issue_reads<ks + 1>(aa, ab, fr[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma(fr[ks & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             wait_reads(fr[(ks + 1) & 1]);
         });
     }
