@@ -9,7 +9,7 @@ import torch
 import async_global_shared_amd as m
 import datagen
 import oracle
-from tests.gpu_util import SENTINEL, full_rows, out_device, same_bits
+from tests.gpu_util import SENTINEL, check_bound, full_rows, out_device, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -152,6 +152,28 @@ def test_odd_sizes_are_refused():
     with pytest.raises(m.MgemmError) as e:
         m.gemm16(A, B)
     assert e.value.status == m.ERR_ARG
+
+
+def test_whole_output_8192_bf16_against_oracle():
+    """The benchmark's 16-bit row (bfloat16, default plan: 256x256 piped S=2)
+    on the full 8192^3 problem: every element of C against the oracle's
+    bound, the whole fp64 product and |A||B| computed on the host cores."""
+    n = 8192
+    A = datagen.matrix16(1, n, n, "bf16")
+    B = datagen.matrix16(2, n, n, "bf16")
+    Ad, Bd = dev16(A, "bf16", extra_rows=0), dev16(B, "bf16", extra_rows=0)
+    assert m.plan16(n, n, n)["tile"] == m._TILE["256x256"]
+    C = m.gemm16(Ad, Bd, stages=2, fill="piped")
+    torch.cuda.synchronize()
+    print("bf16 8192^3 default plan done; oracle on the whole product", flush=True)
+    # every bfloat16 value is exact in fp32, so the fp32 GEMM oracle on the
+    # inputs decoded once (by the oracle's own decoder, tabulated) forms the
+    # same fp64 sums as its 16-bit GEMM, in the same order, at the fp32
+    # oracle's speed
+    table = np.array([oracle.decode16(b, "bf16") for b in range(1 << 16)])
+    Af, Bf = table[A].astype(np.float32), table[B].astype(np.float32)
+    assert np.array_equal(Af, table[A]) and np.array_equal(Bf, table[B])
+    check_bound(C.cpu().numpy(), Af, Bf, what="bf16 8192^3 piped S=2 (whole output)")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
