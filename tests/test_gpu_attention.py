@@ -188,8 +188,9 @@ def test_refused_arguments():
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_full_size(fmt):
     """B = H = 16, Sq = Sk = 4096, D = 128, in the benchmark's launch
-    configuration: sampled heads and rows against the oracle, bit identity
-    across fills and depths on the whole output."""
+    configuration: nine whole heads (every query row; a different head index
+    in each of nine batches, the corners included) against the oracle, bit
+    identity across fills and depths on the whole output."""
     B, H, S, D = 16, 16, 4096, 128
     Q, K, V = (dev_qkv(s, B, H, S, D, fmt) for s in (21, 22, 23))
     ref = m.attention(Q, K, V, stages=2, fill="piped")
@@ -199,8 +200,9 @@ def test_full_size(fmt):
         m.attention(Q, K, V, other, stages=St, fill=fill)
         torch.cuda.synchronize()
         assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), (fmt, fill, St)
-    rows = np.unique(np.r_[0, 1, 127, 128, S - 1, np.linspace(0, S - 1, 10).astype(int)])
-    check(ref, Q, K, V, fmt, D ** -0.5, f"{fmt} full size", heads=[(0, 0), (7, 11), (15, 15)], rows=rows)
+    heads = [(0, 0), (15, 15)] + [(b, (5 * b + 3) % H) for b in range(1, 15, 2)]
+    print(f"{fmt} full size: oracle on {len(heads)} whole heads", flush=True)
+    check(ref, Q, K, V, fmt, D ** -0.5, f"{fmt} full size", heads=heads)
 
 
 # ---- full-size slice sentinels -------------------------------------------------------
