@@ -5,6 +5,8 @@ on every depth. Each result is checked against the oracle (its bound; the copy
 bitwise), bits are compared across fills and depths, and nothing outside the
 output may change. Sizes stay small enough for the oracle to finish in
 seconds, but cross tile, slice and ragged-edge boundaries."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -20,13 +22,16 @@ from tests.test_gpu_gemm16 import check16, dev16, fits
 pytestmark = pytest.mark.gpu
 
 SEED = 20261202
+# cases per operation; MGEMM_RANDOM_CASES widens the sweep (e.g. 1096)
+CASES = range(int(os.environ.get("MGEMM_RANDOM_CASES", "16")))
+PLAIN_CASES = CASES if "MGEMM_RANDOM_CASES" in os.environ else range(8)
 
 
 def _rng(case):
     return np.random.default_rng([SEED, case])
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", CASES)
 def test_fp32_gemm_random(case):
     rng = _rng(case)
     M, N, K = (int(x) for x in rng.integers(1, 600, size=3))
@@ -53,7 +58,7 @@ def test_fp32_gemm_random(case):
                     assert same_bits(C, ref), (what, compute, tile, fill, S)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", CASES)
 def test_gemm16_random(case):
     rng = _rng(100 + case)
     fmt = ("bf16", "f16")[case % 2]
@@ -84,7 +89,7 @@ def test_gemm16_random(case):
                     assert same_bits(C, ref), (what, tile, fill, S)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", CASES)
 def test_attention_random(case):
     rng = _rng(200 + case)
     fmt = ("bf16", "f16")[case % 2]
@@ -118,7 +123,7 @@ def test_attention_random(case):
                 assert torch.equal(O.view(torch.int32), ref.view(torch.int32)), (what, fill, S)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", CASES)
 def test_tile_copy_random(case):
     rng = _rng(300 + case)
     rows, cols = (int(x) for x in rng.integers(1, 900, size=2))
@@ -136,7 +141,7 @@ def test_tile_copy_random(case):
         assert np.all(full[:, cols:] == SENTINEL), (case, rows, cols, S)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", PLAIN_CASES)
 def test_plain_copy_random(case):
     """The plain copy (the tile copy's ceiling) moves the same bytes, on
     aligned (16-byte lanes) and misaligned (4-byte lanes) layouts, and
