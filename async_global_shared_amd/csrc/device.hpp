@@ -1169,16 +1169,15 @@ __global__ void __launch_bounds__(kThreads) zero_kernel(float *C, int M, int N, 
 // ---- pipelined tile copy -----------------------------------------------------------
 //
 // dst = src through an S-slot ring of 64 x 64 fp32 LDS tiles. Of the block's
-// 8 waves, waves 0-3 only fill (asynchronous global -> LDS, non-temporal:
-// the data is used once) and waves 4-7 only drain (LDS -> VGPR -> global,
-// non-temporal stores). Keeping stores out of the filling waves keeps their
-// vmcnt a pure count of their own fills, so the ring's waits are exact.
-// Block b copies runs b, b + G, b + 2G, ... (G = grid size) of R consecutive
-// tiles; the launch makes G the number of runs (one run per block), so the
-// blocks in flight, dispatched in order, sweep one window of memory.
-constexpr int kCopyWaves = 8;
-constexpr int kCopyFillWaves = 4;
-constexpr int kCopyThreads = 64 * kCopyWaves;
+// WAVES waves (8 or 16), the first half only fill (asynchronous global -> LDS,
+// non-temporal: the data is used once) and the second half only drain (LDS
+// -> VGPR -> global, non-temporal stores). Keeping stores out of the filling
+// waves keeps their vmcnt a pure count of their own fills, so the ring's
+// waits are exact. Block b copies runs b, b + G, b + 2G, ... (G = grid size)
+// of R consecutive tiles; the launch makes G the number of runs (one run per
+// block), so the blocks in flight, dispatched in order, sweep one window of
+// memory.
+constexpr int kCopyWavesMax = 16;
 constexpr int kAuxNonTemporal = 2; // buffer load cache-policy bit: streaming
 
 struct CopyArgs {
@@ -1192,10 +1191,11 @@ struct CopyArgs {
 
 using CopyLayout = Layout<64, 64, SwzNone>;
 
-template <int W, bool VST>
+template <int W, bool VST, int WAVES>
 struct CopyOps {
+    static_assert(WAVES == 8 || WAVES == 16, "copy block");
     static constexpr int SLOT = CopyLayout::BYTES;
-    static constexpr int PW = kCopyFillWaves;
+    static constexpr int PW = WAVES / 2;
     using OP = Operand<CopyLayout, W, PW>;
     CopyArgs a;
     OP op;
@@ -1237,7 +1237,7 @@ struct CopyOps {
         int r0, c0;
         coords(t, r0, c0);
         const unsigned char *base = smem + slot * SLOT;
-        constexpr int CW = kCopyWaves - PW;
+        constexpr int CW = WAVES - PW;
         static_assert(CopyLayout::CHUNKS % (64 * CW) == 0, "whole chunks per draining wave");
         constexpr int PER = CopyLayout::CHUNKS / (64 * CW);
         const int cw = wave - PW; // drains chunk positions [cw*PER*64, (cw+1)*PER*64)
@@ -1266,9 +1266,9 @@ struct CopyOps {
     }
 };
 
-template <int S, int W, bool VST>
-__global__ void __launch_bounds__(kCopyThreads) tile_copy_kernel(CopyArgs a) {
-    using Ops = CopyOps<W, VST>;
+template <int S, int W, bool VST, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) tile_copy_kernel(CopyArgs a) {
+    using Ops = CopyOps<W, VST, WAVES>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[S * Ops::SLOT];
     Ops ops;
     ops.a = a;

@@ -220,10 +220,14 @@ MG_GEMM16_CFG(CfgH256x128<false>)
 MG_GEMM16_CFG(CfgH256x256<true>)
 MG_GEMM16_CFG(CfgH256x256<false>)
 #define MG_COPY_INST(S)                                                                                  \
-    template __global__ void mgemm::tile_copy_kernel<S, 16, true>(mgemm::CopyArgs);                      \
-    template __global__ void mgemm::tile_copy_kernel<S, 16, false>(mgemm::CopyArgs);                     \
-    template __global__ void mgemm::tile_copy_kernel<S, 4, true>(mgemm::CopyArgs);                       \
-    template __global__ void mgemm::tile_copy_kernel<S, 4, false>(mgemm::CopyArgs);
+    template __global__ void mgemm::tile_copy_kernel<S, 16, true, 8>(mgemm::CopyArgs);                   \
+    template __global__ void mgemm::tile_copy_kernel<S, 16, false, 8>(mgemm::CopyArgs);                  \
+    template __global__ void mgemm::tile_copy_kernel<S, 4, true, 8>(mgemm::CopyArgs);                    \
+    template __global__ void mgemm::tile_copy_kernel<S, 4, false, 8>(mgemm::CopyArgs);                   \
+    template __global__ void mgemm::tile_copy_kernel<S, 16, true, 16>(mgemm::CopyArgs);                  \
+    template __global__ void mgemm::tile_copy_kernel<S, 16, false, 16>(mgemm::CopyArgs);                 \
+    template __global__ void mgemm::tile_copy_kernel<S, 4, true, 16>(mgemm::CopyArgs);                   \
+    template __global__ void mgemm::tile_copy_kernel<S, 4, false, 16>(mgemm::CopyArgs);
 template __global__ void mgemm::plain_copy_kernel<16>(mgemm::PlainCopyArgs);
 template __global__ void mgemm::plain_copy_kernel<4>(mgemm::PlainCopyArgs);
 MG_COPY_INST(1)
@@ -272,21 +276,26 @@ const void *gemm_kernel(int S, int fill, int W) {
     return W == 16 ? gemm_kernel_w<Cfg, 16>(S, fill) : gemm_kernel_w<Cfg, 4>(S, fill);
 }
 
-template <int S>
+template <int S, int WAVES>
 const void *ck(int W, bool vst) {
     if (W == 16)
-        return vst ? (const void *)&tile_copy_kernel<S, 16, true> : (const void *)&tile_copy_kernel<S, 16, false>;
-    return vst ? (const void *)&tile_copy_kernel<S, 4, true> : (const void *)&tile_copy_kernel<S, 4, false>;
+        return vst ? (const void *)&tile_copy_kernel<S, 16, true, WAVES>
+                   : (const void *)&tile_copy_kernel<S, 16, false, WAVES>;
+    return vst ? (const void *)&tile_copy_kernel<S, 4, true, WAVES> : (const void *)&tile_copy_kernel<S, 4, false, WAVES>;
 }
-const void *copy_kernel(int S, int W, bool vst) {
+template <int WAVES>
+const void *copy_kernel_w(int S, int W, bool vst) {
     switch (S) {
-    case 1: return ck<1>(W, vst);
-    case 2: return ck<2>(W, vst);
-    case 3: return ck<3>(W, vst);
-    case 4: return ck<4>(W, vst);
-    case 5: return ck<5>(W, vst);
-    default: return ck<6>(W, vst);
+    case 1: return ck<1, WAVES>(W, vst);
+    case 2: return ck<2, WAVES>(W, vst);
+    case 3: return ck<3, WAVES>(W, vst);
+    case 4: return ck<4, WAVES>(W, vst);
+    case 5: return ck<5, WAVES>(W, vst);
+    default: return ck<6, WAVES>(W, vst);
     }
+}
+const void *copy_kernel(int S, int W, bool vst, int waves) {
+    return waves == 16 ? copy_kernel_w<16>(S, W, vst) : copy_kernel_w<8>(S, W, vst);
 }
 
 const void *select_gemm(const mgemm_plan_t &p) {
@@ -702,12 +711,12 @@ void trace_attention_fill(FillRecorder &rec) {
     trace_operand<typename C::OV, typename C::LV, W>(rec, 1, C::LK::BYTES, Tile::WAVES, Tile::WAVES, all);
 }
 
-template <int W>
+template <int W, int WAVES>
 void trace_copy_fill(FillRecorder &rec) {
-    using Ops = CopyOps<W, true>;
+    using Ops = CopyOps<W, true, WAVES>;
     auto producer = [](int w) { return w < Ops::PW; };
     rec.put(-1, Ops::SLOT, CopyLayout::kRows, CopyLayout::kCols, 0, 0);
-    trace_operand<typename Ops::OP, CopyLayout, W>(rec, 0, 0, kCopyWaves, Ops::PW, producer);
+    trace_operand<typename Ops::OP, CopyLayout, W>(rec, 0, 0, WAVES, Ops::PW, producer);
 }
 
 template <int W, bool PIPED>
@@ -726,9 +735,14 @@ bool fill_trace_kind(int kind, FillRecorder &rec) {
     case 10:
         if (!PIPED)
             return false;
-        trace_copy_fill<W>(rec);
+        trace_copy_fill<W, 8>(rec);
         return true;
     case 11: trace_gemm_fill<CfgMfma64K<64>, W, PIPED>(rec); return true;
+    case 12:
+        if (!PIPED)
+            return false;
+        trace_copy_fill<W, 16>(rec);
+        return true;
     default: return false;
     }
 }
@@ -884,10 +898,18 @@ int mgemm_tile_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, f
     // G-th run of 4 (resp. 1) tiles 5.78 / 5.89; runs of 4 in this grid
     // 5.98 / 5.87.
     a.run_log2 = stages >= 2 ? 1 : 0;
-    const void *fn = copy_kernel(stages, W, vst);
+    // Blocks of 16 waves (8 filling, 8 draining) or 8 (4 + 4). Measured on
+    // the 1 GiB copy (TB/s, 8 / 16 waves): S=2 faster with 16 at every tile-row
+    // width from 1 to 1024 tiles (16384-wide 5.96 / 6.34, 64-wide 6.14 /
+    // 6.30); S=3 faster with 16 from 4 tiles per tile-row up (16384-wide
+    // 6.09 / 6.40, 1024-wide 6.19 / 6.53), slower with one or two (64-wide
+    // 6.12 / 5.62, 128-wide 6.15 / 5.63); S=1 (one tile per block) faster
+    // with 8 on contiguous tiles (64-wide 6.34 / 6.00).
+    const int waves = (stages == 2 || (stages >= 3 && a.tcols > 2)) ? 16 : 8;
+    const void *fn = copy_kernel(stages, W, vst, waves);
     const int64_t runs = (ntiles + (1 << a.run_log2) - 1) >> a.run_log2;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    return launch(fn, (int)runs, &a, s, kCopyThreads);
+    return launch(fn, (int)runs, &a, s, 64 * waves);
 }
 
 int mgemm_plain_copy(int64_t rows, int64_t cols, const float *src, int64_t lds, float *dst, int64_t ldd,

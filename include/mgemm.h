@@ -288,8 +288,9 @@ int mgemm_ring_trace(int kind, int stages, int fill_mode, int slices, int *event
  * destination in the LDS slot). kind: 0 fp32 VALU 64x64, 1 VALU 128x128,
  * 2 fp32 MFMA 64x64 with a 32-k slice, 3 MFMA 128x128, 4 MFMA 256x128,
  * 5 16-bit 128x128, 6 16-bit 256x128, 7 16-bit 256x256, 8 attention head
- * dim 64, 9 head dim 128, 10 tile copy (MGEMM_FILL_PIPED only), 11 fp32
- * MFMA 64x64 with a 64-k slice; load_bytes 16 or 4;
+ * dim 64, 9 head dim 128, 10 tile copy in blocks of 8 waves (MGEMM_FILL_PIPED
+ * only), 11 fp32 MFMA 64x64 with a 64-k slice, 12 tile copy in blocks of 16
+ * waves (MGEMM_FILL_PIPED only); load_bytes 16 or 4;
  * fill_mode MGEMM_FILL_SYNC (register-staged) or MGEMM_FILL_PIPED.
  * Events are 6 ints written to events[0 .. 6*cap). The first is a header
  * {-1, slot bytes, rows and 32-bit columns of operand 0, rows and columns of

@@ -333,7 +333,8 @@ def test_split_ring_schedule(S):
 
 FILL_KINDS = {0: "fp32 VALU 64", 1: "fp32 VALU 128", 2: "fp32 MFMA 64 (32-k slice)", 3: "fp32 MFMA 128",
               4: "fp32 MFMA 256x128", 5: "16-bit 128", 6: "16-bit 256x128", 7: "16-bit 256x256", 8: "attention D64",
-              9: "attention D128", 10: "tile copy", 11: "fp32 MFMA 64 (64-k slice)"}
+              9: "attention D128", 10: "tile copy, 8 waves", 11: "fp32 MFMA 64 (64-k slice)",
+              12: "tile copy, 16 waves"}
 
 
 @pytest.mark.parametrize("kind", sorted(FILL_KINDS))
@@ -344,7 +345,7 @@ def test_fill_map_covers_the_slot_once(kind, W, fill):
     filling-wave rules: every byte of the LDS slot is written exactly once,
     every element of each operand's slice is fetched exactly once, and each
     lands where the compute side's layout reads it."""
-    if kind == 10 and fill == 0:
+    if kind in (10, 12) and fill == 0:
         assert m.lib().mgemm_fill_trace(kind, W, fill, None, 0) == m.ERR_ARG
         return
     (slot, r0, c0, r1, c1), ev = m.mgemm_fill_trace(kind, W, fill)
@@ -362,8 +363,8 @@ def test_fill_map_covers_the_slot_once(kind, W, fill):
     waves = {w for _, w, *_ in ev}
     if kind == 7 and fill == 1 and W == 16:
         assert waves == {0, 1, 2, 3}  # the 8-wave tile's asynchronous ring fills from one wave per SIMD
-    elif kind == 10:
-        assert waves == {0, 1, 2, 3}  # the copy's filling waves
+    elif kind in (10, 12):
+        assert waves == set(range(4 if kind == 10 else 8))  # the copy's filling waves: the block's first half
     else:
         assert waves == set(range(8 if kind in (7, 8, 9) else 4))
 
