@@ -224,8 +224,10 @@ def attention_bound(ref: AttnRef, fmt: str, scale: float) -> np.ndarray:
     at most delta moves each softmax weight by a factor within
     exp(+-2 delta), so O by at most 2 delta sum_j w_j |v_jc|, taken twice.
     The last term covers probabilities too small for a relative error: the
-    kernels' probabilities lie in [0, 1] with a row sum of at least 1 (the
-    row maximum contributes 2^0), and each key's rounded probability is off
+    kernels' probabilities are taken against a running reference at most 8
+    (log2 units) below the row maximum, so they lie in [0, 2^8] with a row
+    sum of at least 1 (the row maximum contributes 2^0 or more), and each
+    key's rounded probability is off
     by at most tau in absolute terms below the format's normal range. For
     bfloat16 (fp32's exponent range) that is fp32 underflow, tau = 2^-125;
     binary16 stops at subnormals spaced 2^-24 (nothing below 2^-25 survives
