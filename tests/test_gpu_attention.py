@@ -109,6 +109,32 @@ def test_every_variant(fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_long_key_sequence(fmt, D):
+    """32805 keys (513 slices, the last one ragged) for 70 queries of two
+    heads: the online softmax over a long ring, every fill and depth that
+    fits, within the bound and bit-identical."""
+    B, H, Sq, Sk = 1, 2, 70, 32805
+    Q = dev_qkv(13, B, H, Sq, D, fmt)
+    K = dev_qkv(14, B, H, Sk, D, fmt)
+    V = dev_qkv(15, B, H, Sk, D, fmt)
+    scale = D ** -0.5
+    ref = None
+    for fill, S in VARIANTS:
+        if not fits(S, fill, D):
+            continue
+        O, buf = out_view(B, H, Sq, D, pad=2)
+        m.attention(Q, K, V, O, scale=scale, stages=S, fill=fill)
+        torch.cuda.synchronize()
+        assert bool(torch.all(buf[..., D:] == SENTINEL)), (fill, S)
+        if ref is None:
+            check(O, Q, K, V, fmt, scale, f"{fmt} D{D} long keys {fill} S{S}")
+            ref = O.clone()
+        else:
+            assert torch.equal(O.view(torch.int32), ref.view(torch.int32)), (fmt, D, fill, S)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_layouts(fmt):
     """(batch, seq, head, dim) storage, misaligned bases (4-byte loads) and a
     padded output give the same bits as contiguous inputs."""

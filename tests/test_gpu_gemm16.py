@@ -116,6 +116,33 @@ def test_few_slices(K):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_long_k(fmt):
+    """K = 32776 (513 slices of 64, the last one ragged) on a ragged 96 x 130 C:
+    every tile, fill and depth that fits, within the bound and bit-identical."""
+    M, N, K = 96, 130, 32776
+    A = datagen.matrix16(11, M, K, fmt)
+    B = datagen.matrix16(12, K, N, fmt)
+    Ad, Bd = dev16(A, fmt), dev16(B, fmt)
+    for tile in TILES16:
+        ref = None
+        for fill in ("sync", "piped"):
+            for S in (1, 2, 3, 4):
+                if not fits(tile, S) or (fill == "sync" and S == 4):
+                    continue
+                Cd = out_device(M, N, N + 2)
+                m.gemm16(Ad, Bd, Cd, stages=S, fill=fill, tile=tile)
+                torch.cuda.synchronize()
+                full = full_rows(Cd)
+                assert np.all(full[:, N:] == SENTINEL), (fmt, tile, fill, S)
+                C = full[:, :N]
+                if ref is None:
+                    check16(C, A, B, fmt, what=f"{fmt} long K {tile}")
+                    ref = C
+                else:
+                    assert same_bits(C, ref), (fmt, tile, fill, S)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_coarse_grid_exact(fmt):
     M, N, K = 384, 256, 1024
     A = datagen.matrix16(3, M, K, fmt, kind="coarse")

@@ -95,6 +95,29 @@ def test_every_variant_ragged(layout):
                         assert same_bits(C, ref), f"{layout} {compute} {tile} {fill} S={S} {ld} != first variant"
 
 
+def test_long_k_many_slices():
+    """K far beyond any ring (65573: 4099 slices of 16 k, 1025 of 64, the last
+    one ragged) on a ragged 70 x 130 C: every tile, fill and depth that fits,
+    within the bound and bit-identical per (compute, tile); C padding untouched."""
+    M, N, K = 70, 130, 65573
+    A, B = _inputs("uniform", M, N, K, seed=7)
+    Ad, Bd = padded_device(A), padded_device(B)
+    for compute, tile in TILES:
+        ref = None
+        for fill in FILLS:
+            for S in STAGES:
+                if not ring_fits(M, N, K, compute=compute, tile=tile, fill=fill, stages=S):
+                    continue
+                full = full_rows(run(Ad, Bd, out_device(M, N), compute=compute, tile=tile, fill=fill, stages=S))
+                assert np.all(full[:, N:] == SENTINEL), f"long K {compute} {tile}: wrote C padding"
+                C = full[:, :N]
+                if ref is None:
+                    check_bound(C, A, B, what=f"long K {compute} {tile} {fill} S={S}")
+                    ref = C
+                else:
+                    assert same_bits(C, ref), f"long K {compute} {tile} {fill} S={S} != first variant"
+
+
 @pytest.mark.parametrize("layout", ["padded_ld", "misaligned"])
 def test_deep_piped_rings(layout):
     """Rings of 4-6 stages (the lesson's exercise sweeps the depth) give the
