@@ -8,6 +8,7 @@ import torch
 
 import async_global_shared_amd as m
 import datagen
+import oracle
 from tests.gpu_util import check_bound, same_bits
 
 pytestmark = pytest.mark.gpu
@@ -172,3 +173,60 @@ def test_copy_one_gib(S, shape):
         m.plain_copy(src, dst)
         torch.cuda.synchronize()
         assert torch.equal(dst.view(torch.int32), src.view(torch.int32))
+
+
+def test_largest_leading_dimension():
+    """The largest leading dimension the library takes, 2^21 - 4 words (8 MiB
+    rows): a 256-row tile's panel then spans nearly the 2^31-byte range its
+    buffer descriptor covers. A (300 x 70) sits in a NaN-poisoned buffer of
+    that row pitch, 2.4 GiB, and C has the same pitch. Every fp32 tile, both
+    fills at depths 1 and 2, within the bound and bit-identical per tile; the
+    16-bit GEMM on the same bytes (2 (2^21 - 4) elements per row) likewise."""
+    M, N, K = 300, 130, 70
+    ld = (1 << 21) - 4
+    A = datagen.matrix("uniform", 41, M, K)
+    B = datagen.matrix("uniform", 42, K, N)
+    abuf = torch.full(((M + 2) * ld,), float("nan"), dtype=torch.float32, device="cuda")
+    Ad = abuf[:M * ld].view(M, ld)[:, :K]
+    Ad.copy_(torch.from_numpy(A))
+    Bd = torch.from_numpy(B).cuda()
+    cbuf = torch.full(((M + 1) * ld,), -1.0, dtype=torch.float32, device="cuda")
+    Cd = cbuf[:M * ld].view(M, ld)[:, :N]
+    for compute, tile in [("valu", "64x64"), ("valu", "128x128"), ("mfma", "64x64"), ("mfma", "128x128"),
+                          ("mfma", "256x128")]:
+        ref = None
+        for fill in ("sync", "piped"):
+            for S in (1, 2):
+                Cd.fill_(float("nan"))
+                m.sgemm(Ad, Bd, Cd, stages=S, fill=fill, compute=compute, tile=tile)
+                torch.cuda.synchronize()
+                C = Cd.cpu().numpy()
+                if ref is None:
+                    check_bound(C, A, B, what=f"ld 2^21-4 {compute} {tile}")
+                    ref = C
+                else:
+                    assert same_bits(C, ref), (compute, tile, fill, S)
+    assert bool(torch.all(cbuf[:M * ld].view(M, ld)[:, N:N + 64] == -1.0)), "C written past N"
+    del abuf, Ad, cbuf, Cd
+
+    fmt = "bf16"
+    A16 = datagen.matrix16(43, M, K, fmt)
+    B16 = datagen.matrix16(44, K, N, fmt)
+    ld16 = 2 * ld
+    a16 = torch.full(((M + 2) * ld16,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Ad16 = a16[:M * ld16].view(M, ld16)[:, :K]
+    Ad16.copy_(torch.from_numpy(A16.view(np.int16)).view(torch.bfloat16))
+    Bd16 = torch.from_numpy(B16.view(np.int16)).cuda().view(torch.bfloat16)
+    ref = None
+    for tile in ("128x128", "256x128", "256x256"):
+        for fill, S in (("sync", 1), ("piped", 2)):
+            C16 = m.gemm16(Ad16, Bd16, stages=S, fill=fill, tile=tile)
+            torch.cuda.synchronize()
+            C = C16.cpu().numpy()
+            if ref is None:
+                want = oracle.gemm16_f64(A16, B16, fmt)
+                bnd = oracle.bound(K, oracle.gemm16_f64(A16, B16, fmt, absolute=True))
+                assert np.all(np.abs(C.astype(np.float64) - want) <= bnd), f"16-bit ld 2(2^21-4) {tile}"
+                ref = C
+            else:
+                assert same_bits(C, ref), (tile, fill, S)
