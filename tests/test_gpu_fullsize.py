@@ -181,7 +181,9 @@ def test_largest_leading_dimension():
     buffer descriptor covers. A (300 x 70) sits in a NaN-poisoned buffer of
     that row pitch, 2.4 GiB, and C has the same pitch. Every fp32 tile, both
     fills at depths 1 and 2, within the bound and bit-identical per tile; the
-    16-bit GEMM on the same bytes (2 (2^21 - 4) elements per row) likewise."""
+    tile copy (S = 1-3) and the plain copy between views of that pitch, byte
+    for byte; the 16-bit GEMM on the same bytes (2 (2^21 - 4) elements per
+    row) within the bound and bit-identical."""
     M, N, K = 300, 130, 70
     ld = (1 << 21) - 4
     A = datagen.matrix("uniform", 41, M, K)
@@ -207,7 +209,19 @@ def test_largest_leading_dimension():
                 else:
                     assert same_bits(C, ref), (compute, tile, fill, S)
     assert bool(torch.all(cbuf[:M * ld].view(M, ld)[:, N:N + 64] == -1.0)), "C written past N"
-    del abuf, Ad, cbuf, Cd
+    # the tile copy and the plain copy between views of that pitch
+    src = abuf[:M * ld].view(M, ld)[:, :N]
+    src.copy_(datagen.normal01_torch(45, M * N, device="cuda").view(M, N))
+    for S in (1, 2, 3, 0):
+        Cd.fill_(float("nan"))
+        if S:
+            m.tile_copy(src, Cd, stages=S)
+        else:
+            m.plain_copy(src, Cd)
+        torch.cuda.synchronize()
+        assert torch.equal(Cd.view(torch.int32), src.view(torch.int32)), f"copy S={S} at ld 2^21-4"
+    assert bool(torch.all(cbuf[:M * ld].view(M, ld)[:, N:N + 64] == -1.0)), "copy wrote past the columns"
+    del abuf, Ad, cbuf, Cd, src
 
     fmt = "bf16"
     A16 = datagen.matrix16(43, M, K, fmt)
