@@ -337,6 +337,22 @@ def oracle_rate(Ad, Bd, budget_s=3.0):
     return {"gflops": round(fl / dt / 1e9, 3), "threads": threads, "rows": rows, "of_rows": M, "s": round(dt, 3)}
 
 
+def copy_oracle_rate(host, nbytes):
+    """The oracle's copy (row memcpy, OpenMP over rows, all host threads) of
+    the same 1 GiB on the host: the best of 3 runs, the bytes checked."""
+    import numpy as np
+    import oracle
+    lib = oracle.load()
+    best = None
+    for _ in range(3):
+        dt, out = oracle.timed_copy(host, lib=lib)
+        best = dt if best is None else min(best, dt)
+    if not np.array_equal(out.view(np.int32), host.view(np.int32)):
+        raise SystemExit("oracle copy changed bytes")
+    return {"s": round(best, 4), "GBps": round(nbytes / best / 1e9, 1), "cores": oracle.num_threads(lib),
+            "what": "oracle_copy_f32 on the host cores, the 16384x16384 view (read + write bytes over time)"}
+
+
 def tables(m, datagen, torch, Ad8, Bd8, Cd8, with_oracle=True):
     """Stage/fill table (GFLOP/s, speedups), VALU variant, tile copy GB/s."""
     res = {}
@@ -412,6 +428,8 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8, with_oracle=True):
     t = timed_launches(lambda: dst.copy_(src), repeats=REPEATS)
     copy["torch_copy_context"] = {"ms": round(t["ms_median"], 4),
                                   "GBps": round(nbytes / (t["ms_median"] * 1e-3) / 1e9, 1)}
+    if with_oracle:
+        copy["oracle"] = copy_oracle_rate(src.view(*COPY_VIEWS[0]).cpu().numpy(), nbytes)
     res["tile_copy_1GiB"] = copy
     del src, dst
     return res

@@ -166,6 +166,18 @@ def timed_gemm_rows(A: np.ndarray, B: np.ndarray, rows: int, lib=None):
     return dt, 2.0 * M * N * K
 
 
+def timed_copy(src: np.ndarray, lib=None):
+    """Run oracle_copy_f32 on the whole of ``src`` into a fresh array and
+    return (seconds, copy). Used only for the CPU baseline of the tile copy."""
+    lib = lib or load()
+    rows, cols = src.shape
+    dst = np.empty((rows, cols), dtype=np.float32)
+    dst.fill(0.0)  # touch every page before the clock starts
+    t0 = time.perf_counter()
+    lib.oracle_copy_f32(rows, cols, _ptr(src), src.strides[0] // 4, _ptr(dst), cols)
+    return time.perf_counter() - t0, dst
+
+
 class AttnRef(NamedTuple):
     """The attention oracle's result and the magnitudes its bound needs."""
     O: np.ndarray     # (..., Sq, Dv) softmax(scale Q K^T) V
