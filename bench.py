@@ -388,6 +388,17 @@ def tables(m, datagen, torch, Ad8, Bd8, Cd8, with_oracle=True):
                     p["time_ratio_piped_over_sync_S1"] = round(p["ms"] / base["ms"], 3)
                 if s and p:
                     p["speedup_vs_sync_same_S"] = round(s["ms"] / p["ms"], 3)
+        # the vendor library's fp32 product on the same operands, as context
+        # (full fp32: TF32-style reduced-precision paths switched off)
+        prev = torch.backends.cuda.matmul.allow_tf32
+        torch.backends.cuda.matmul.allow_tf32 = False
+        try:
+            t = timed_launches(lambda: torch.mm(A, B, out=C), repeats=REPEATS)
+        finally:
+            torch.backends.cuda.matmul.allow_tf32 = prev
+        row["torch_mm_fp32_context"] = {"ms": round(t["ms_median"], 4),
+                                        "gflops": round(flop / (t["ms_median"] * 1e-3) / 1e9, 1),
+                                        "pct_peak": round(100 * flop / (t["ms_median"] * 1e-3) / 1e12 / 157.3, 2)}
         if with_oracle and n != big:  # the full size's oracle rate is the cpu_baseline record
             row["oracle"] = oracle_rate(A, B)
         gemm[str(n)] = row
