@@ -95,24 +95,37 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
     }
 
     if (tile == MGEMM_TILE_AUTO) {
-        // 64x64 or 128x128, whichever has the least estimated time: each of
-        // the 256 CUs works through ceil(blocks / 256) tiles, each costing
-        // its area over the tile's relative throughput (8192^3, piped S=2:
+        // 64x64, 128x128 or (below) 256x128, whichever has the least
+        // estimated time: each of the 256 CUs works through ceil(blocks /
+        // 256) tiles, each costing its area over the tile's relative
+        // throughput (8192^3, piped S=2:
         // 64x64 runs at 0.90 (VALU) / 0.91 (MFMA) of 128x128), slowed where
         // few blocks share a CU: one wave issues a dependence-free FMA only
         // every few cycles, so the VALU tile needs several waves per SIMD
         // (measured 1.80x slower with one, 1.13x with two, 1.05x with three);
         // the MFMA tile 1.1x with one. Resident blocks are capped by the
         // ring's LDS and by the kernel's registers. Ties keep 128x128.
+        // For the asynchronous ring of two or more stages with MFMA, the
+        // 256x128 tile (three resident) runs at the 128x128 tile's rate or
+        // above (TFLOP/s, same box, 256x128 vs 128x128: piped S=2 4096^3
+        // 145.6 vs 145.2, 8192^3 147.8 vs 147.8; S=3 143.8 vs 142.2 and
+        // 148.4 vs 146.1) and fetches about a third of the HBM bytes at
+        // 8192^3, so it takes ties there (1.01). Elsewhere it loses (sync S=3
+        // 124.9 vs 135.1 and 126.8 vs 140.0; piped S=1 at 4096^3 135.6 vs
+        // 142.6) and is not considered. Every MFMA tile gives the same bits
+        // (each accumulator sees the k values in the same order).
         const bool valu = compute == MGEMM_COMPUTE_VALU;
         struct Cand {
             int tile, bm, bn, cap;
             double eff;
         };
         const Cand cands[] = {{MGEMM_TILE_128x128, 128, 128, valu ? 4 : 5, 1.0},
-                              {MGEMM_TILE_64x64, 64, 64, 8, valu ? 0.90 : 0.91}};
+                              {MGEMM_TILE_64x64, 64, 64, 8, valu ? 0.90 : 0.91},
+                              {MGEMM_TILE_256x128, 256, 128, 3, 1.01}};
         double best = 0.0;
         for (const Cand &c : cands) {
+            if (c.tile == MGEMM_TILE_256x128 && (valu || fill != MGEMM_FILL_PIPED || stages < 2))
+                continue;
             const int64_t blocks = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
             const int64_t per_cu = (blocks + 255) / 256;
             const int slot = (c.bm + c.bn) * kBK * 4;

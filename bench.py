@@ -95,7 +95,8 @@ def parse():
 
 def profile_mode(args):
     """Launches for counter collection, `steps` of each, no timing: the timed
-    GEMM, its VALU twin, the ragged and tall-skinny GEMMs (MFMA, piped S=2),
+    GEMM, its VALU twin, the automatic MFMA plan of the same problem (the
+    256x128 tile), the ragged and tall-skinny GEMMs (MFMA, piped S=2),
     the 1 GiB tile copy in both array views, the plain
     1 GiB copy (mgemm_plain_copy, the calibration kernel for hardware byte
     counters), the 16-bit GEMM and the attention kernel in their default
@@ -113,6 +114,11 @@ def profile_mode(args):
             m.sgemm(Ad, Bd, Cd, stages=args.stages, fill="piped", compute=compute, tile="128x128")
         torch.cuda.synchronize()
         print(f"profile: {args.steps} x sgemm {n}^3 {compute} piped S={args.stages}", flush=True)
+    for _ in range(args.steps):
+        m.sgemm(Ad, Bd, Cd, stages=args.stages, fill="piped", compute="mfma")
+    torch.cuda.synchronize()
+    print(f"profile: {args.steps} x sgemm {n}^3 mfma piped S={args.stages}, automatic plan "
+          f"{m.plan(n, n, n, stages=args.stages, compute='mfma')}", flush=True)
     del Ad, Bd, Cd
     for name, M, N, K in CONFIG5:
         A = datagen.uniform_pm1_torch(datagen.SEED_A, M * K, device="cuda").view(M, K)

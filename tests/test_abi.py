@@ -107,8 +107,11 @@ def test_plan_tiles_loaders_and_lds():
     p = m.plan(256, 256, 256)
     assert (p["bm"], p["bn"], p["bk"], p["threads"], p["blocks"]) == (64, 64, 16, 256, 16)
     assert p["load_bytes"] == 16 and p["slices"] == 16
-    p = m.plan(4096, 4096, 4096, compute="mfma", stages=3)
+    p = m.plan(4096, 4096, 4096, compute="mfma", stages=3, tile="128x128")
     assert (p["bm"], p["blocks"], p["lds_bytes"], p["loads_per_slice"], p["max_vmcnt"]) == (128, 1024, 49152, 4, 4)
+    p = m.plan(4096, 4096, 4096, compute="mfma", stages=3)  # automatic: 256x128 on the 2+ stage ring
+    assert (p["bm"], p["bn"], p["blocks"], p["lds_bytes"], p["loads_per_slice"], p["max_vmcnt"]) == \
+        (256, 128, 512, 73728, 6, 6)
     # ragged, misaligned leading dimensions -> 4-byte loads
     p = m.plan(4099, 3001, 1537, stages=3, tile="128x128", lda=1537, ldb=3001, ldc=3001)
     assert p["load_bytes"] == 4 and p["bm"] == 128 and p["blocks"] == 33 * 24 and p["slices"] == 97
@@ -139,9 +142,18 @@ AUTO_FP32 = {(4099, 3001, 1537): 64, (16384, 64, 4096): 64, (2048, 2048, 2048): 
 @pytest.mark.parametrize("compute", ["valu", "mfma"])
 def test_auto_fp32_tile(compute):
     for (M, N, K), edge in AUTO_FP32.items():
-        for S in (1, 2, 3):
-            p = m.plan(M, N, K, stages=S, compute=compute)
-            assert (p["bm"], p["bn"]) == (edge, edge), (compute, M, N, K, S)
+        for fill in ("sync", "piped"):
+            for S in (1, 2, 3):
+                p = m.plan(M, N, K, stages=S, fill=fill, compute=compute)
+                want = (edge, edge)
+                # MFMA on the asynchronous ring of 2+ stages: 256x128 where
+                # 128x128 would be chosen (same rate, a third of the HBM bytes)
+                if compute == "mfma" and fill == "piped" and S >= 2 and edge == 128:
+                    want = (256, 128)
+                assert (p["bm"], p["bn"]) == want, (compute, fill, M, N, K, S)
+    # the warp-specialised ring keeps 128x128
+    p = m.plan(8192, 8192, 8192, stages=2, fill="piped_ws", compute="mfma")
+    assert (p["bm"], p["bn"]) == (128, 128)
     # the ABI's plain entry point plans with the VALU tile and the same choice
     st, pl = m.mgemm_plan_sgemm(4099, 3001, 1537, A0, 1537, B0, 3001, C0, 3001, 2, 1, 0, 0, 0)
     assert st == m.OK and pl.bm == 64
