@@ -58,7 +58,10 @@ struct mgemm_plan; /* defined below (mgemm_plan_t) */
 #define MGEMM_COMPUTE_MFMA 1 /* v_mfma_f32_32x32x2_f32 wave tiles */
 
 /* tile: block tile of C (BM x BN, K slice 16 unless noted, 256 threads). */
-#define MGEMM_TILE_AUTO 0      /* 64x64 or 128x128, whichever a wave model of the CUs estimates faster */
+#define MGEMM_TILE_AUTO 0      /* 64x64 or 128x128, whichever a wave model of the CUs estimates faster;
+                                  with MFMA on the asynchronous ring of 2+ stages also 256x128, which
+                                  takes ties (same rate, fewer HBM bytes). Every tile of one compute
+                                  kind gives the same bits, so the choice never changes C. */
 #define MGEMM_TILE_64x64 1   /* VALU: 4x4 micro-tile per thread (the pages' shape); MFMA: one 32x32
                                 tile per wave, K slice 64 where the grid gives each of 256 CUs one
                                 block at most, else 32 (chosen from the shape alone) */
@@ -87,8 +90,8 @@ struct mgemm_plan; /* defined below (mgemm_plan_t) */
  * piped keeps stages-1 slices in flight during compute. fill_mode is
  * MGEMM_FILL_SYNC, MGEMM_FILL_PIPED or MGEMM_FILL_PIPED_WS ("A study on CUDA
  * async memcpy", producer/consumer pipeline). Uses the VALU compute tile and the
- * automatic tile and loader choice. For a fixed (shape, compute, tile), every
- * (stages, fill_mode, loader) gives bit-identical C. M == 0 or N == 0: no-op.
+ * automatic tile and loader choice. For a fixed (shape, compute), every
+ * (tile, stages, fill_mode, loader) gives bit-identical C. M == 0 or N == 0: no-op.
  * K == 0: C[0:M, 0:N] = +0. Cells of C outside M x N are never written.
  * MGEMM_FILL_PIPED_WS guards each of its LDS-counter waits with a bounded
  * spin (about 2^22 polls); a block whose wait runs out, which a correct

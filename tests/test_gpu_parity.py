@@ -95,6 +95,30 @@ def test_every_variant_ragged(layout):
                         assert same_bits(C, ref), f"{layout} {compute} {tile} {fill} S={S} {ld} != first variant"
 
 
+@pytest.mark.parametrize("layout", ["aligned", "misaligned", "many_tiles"])
+def test_tiles_agree_bitwise(layout):
+    """For one compute kind every block tile gives the same bits: each C
+    element is one fma chain over k ascending (VALU) or one MFMA sequence in
+    the absolute k order (MFMA), however the tile and its K slice cut the
+    problem; so the automatic tile choice never changes a result."""
+    M, N, K, lda, ldb, ldc, (oa, ob, oc) = LAYOUTS[layout]
+    A, B = _inputs("uniform", M, N, K, seed=12)
+    Ad = padded_device(A, lda, offset=oa)
+    Bd = padded_device(B, ldb, offset=ob)
+    for compute in ("valu", "mfma"):
+        ref = None
+        for c, tile in TILES:
+            if c != compute:
+                continue
+            for fill, S in (("sync", 1), ("piped", 2)):
+                C = full_rows(run(Ad, Bd, out_device(M, N, ldc, offset=oc), compute=compute, tile=tile, fill=fill,
+                                  stages=S))[:, :N]
+                if ref is None:
+                    ref = C
+                else:
+                    assert same_bits(C, ref), f"{layout} {compute} {tile} {fill} S={S} differs from the first tile"
+
+
 def test_long_k_many_slices():
     """K far beyond any ring (65573: 4099 slices of 16 k, 1025 of 64, the last
     one ragged) on a ragged 70 x 130 C: every tile, fill and depth that fits,
