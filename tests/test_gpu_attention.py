@@ -134,6 +134,31 @@ def test_long_key_sequence(fmt, D):
             assert torch.equal(O.view(torch.int32), ref.view(torch.int32)), (fmt, D, fill, S)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_many_heads(D):
+    """5 x 37 (batch, head) pairs of 300 queries: 370 blocks, not a multiple
+    of the 8 XCDs, so the block -> (batch, head, query block) map runs with a
+    remainder; (batch, seq, head, dim) storage. Six heads against the oracle,
+    every head bit-identical across fills and depths."""
+    fmt, B, H, Sq, Sk = "bf16", 5, 37, 300, 130
+    Q = dev_qkv(16, B, H, Sq, D, fmt, layout="bshd")
+    K = dev_qkv(17, B, H, Sk, D, fmt, layout="bshd")
+    V = dev_qkv(18, B, H, Sk, D, fmt, layout="bshd")
+    assert m.plan_attention(B, H, Sq, Sk, D)["blocks"] == B * H * 2
+    scale = D ** -0.5
+    ref = None
+    for fill, S in (("sync", 1), ("piped", 2), ("piped", 3)):
+        O, buf = out_view(B, H, Sq, D, pad=1)
+        m.attention(Q, K, V, O, scale=scale, stages=S, fill=fill)
+        torch.cuda.synchronize()
+        assert bool(torch.all(buf[..., D:] == SENTINEL)), (fill, S)
+        if ref is None:
+            check(O, Q, K, V, fmt, scale, f"many heads D{D}", heads=[(0, 0), (0, 36), (2, 17), (3, 5), (4, 0), (4, 36)])
+            ref = O.clone()
+        else:
+            assert torch.equal(O.view(torch.int32), ref.view(torch.int32)), (D, fill, S)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_layouts(fmt):
     """(batch, seq, head, dim) storage, misaligned bases (4-byte loads) and a
