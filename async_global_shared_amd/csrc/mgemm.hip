@@ -95,37 +95,24 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
     }
 
     if (tile == MGEMM_TILE_AUTO) {
-        // 64x64, 128x128 or (below) 256x128, whichever has the least
-        // estimated time: each of the 256 CUs works through ceil(blocks /
-        // 256) tiles, each costing its area over the tile's relative
-        // throughput (8192^3, piped S=2:
+        // 64x64 or 128x128, whichever has the least estimated time: each of
+        // the 256 CUs works through ceil(blocks / 256) tiles, each costing
+        // its area over the tile's relative throughput (8192^3, piped S=2:
         // 64x64 runs at 0.90 (VALU) / 0.91 (MFMA) of 128x128), slowed where
         // few blocks share a CU: one wave issues a dependence-free FMA only
         // every few cycles, so the VALU tile needs several waves per SIMD
         // (measured 1.80x slower with one, 1.13x with two, 1.05x with three);
         // the MFMA tile 1.1x with one. Resident blocks are capped by the
         // ring's LDS and by the kernel's registers. Ties keep 128x128.
-        // For the asynchronous ring of two or more stages with MFMA, the
-        // 256x128 tile (three resident) runs at the 128x128 tile's rate or
-        // above (TFLOP/s, same box, 256x128 vs 128x128: piped S=2 4096^3
-        // 145.6 vs 145.2, 8192^3 147.8 vs 147.8; S=3 143.8 vs 142.2 and
-        // 148.4 vs 146.1) and fetches about a third of the HBM bytes at
-        // 8192^3, so it takes ties there (1.01). Elsewhere it loses (sync S=3
-        // 124.9 vs 135.1 and 126.8 vs 140.0; piped S=1 at 4096^3 135.6 vs
-        // 142.6) and is not considered. Every MFMA tile gives the same bits
-        // (each accumulator sees the k values in the same order).
         const bool valu = compute == MGEMM_COMPUTE_VALU;
         struct Cand {
             int tile, bm, bn, cap;
             double eff;
         };
         const Cand cands[] = {{MGEMM_TILE_128x128, 128, 128, valu ? 4 : 5, 1.0},
-                              {MGEMM_TILE_64x64, 64, 64, 8, valu ? 0.90 : 0.91},
-                              {MGEMM_TILE_256x128, 256, 128, 3, 1.01}};
+                              {MGEMM_TILE_64x64, 64, 64, 8, valu ? 0.90 : 0.91}};
         double best = 0.0;
         for (const Cand &c : cands) {
-            if (c.tile == MGEMM_TILE_256x128 && (valu || fill != MGEMM_FILL_PIPED || stages < 2))
-                continue;
             const int64_t blocks = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
             const int64_t per_cu = (blocks + 255) / 256;
             const int slot = (c.bm + c.bn) * kBK * 4;
@@ -138,6 +125,23 @@ int plan_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, cons
                 tile = c.tile;
                 best = t;
             }
+        }
+        // Where 128x128 wins with MFMA on the asynchronous ring of 2 or 3
+        // stages, the 256x128 tile (two resident per CU) takes over when
+        // every CU gets an even number of its tiles: it then runs at the
+        // 128x128 rate or above and fetches about a third of the HBM bytes
+        // (8192^3: 3.6 against 9.5 GB). With an odd or uneven count its last
+        // block runs alone on the CU, one wave per SIMD (measured, N = K =
+        // 8192, TFLOP/s, 256x128 S=2 / 128x128 S=2: 2, 4, 6, 8, 10, 12 tiles
+        // per CU 147.3 / 146.2, 147.9 / 147.7, 148.2 / 147.4, 148.2 / 148.0,
+        // 148.1 / 147.9, 148.0 / 148.0; 3, 5, 7, 9, 11 tiles 110 / 146, 125 /
+        // 147, 135 / 147, 143 / 147, 146 / 146; S=3 148.3-148.8 against
+        // 145.0-146.6 for 128x128 S=3 at 6-12). Every MFMA tile gives the
+        // same bits (each accumulator sees the k values in the same order).
+        if (tile == MGEMM_TILE_128x128 && !valu && fill == MGEMM_FILL_PIPED && (stages == 2 || stages == 3)) {
+            const int64_t big = ((M + 255) / 256) * ((N + 127) / 128);
+            if (big >= 512 && big % 512 == 0)
+                tile = MGEMM_TILE_256x128;
         }
     }
     const int bm = tile == MGEMM_TILE_256x128 ? 256 : tile == MGEMM_TILE_128x128 ? 128 : 64;

@@ -59,9 +59,10 @@ struct mgemm_plan; /* defined below (mgemm_plan_t) */
 
 /* tile: block tile of C (BM x BN, K slice 16 unless noted, 256 threads). */
 #define MGEMM_TILE_AUTO 0      /* 64x64 or 128x128, whichever a wave model of the CUs estimates faster;
-                                  with MFMA on the asynchronous ring of 2+ stages also 256x128, which
-                                  takes ties (same rate, fewer HBM bytes). Every tile of one compute
-                                  kind gives the same bits, so the choice never changes C. */
+                                  with MFMA on the asynchronous ring of 2 or 3 stages, 256x128 in place
+                                  of 128x128 when every CU gets an even number of its tiles (same rate,
+                                  fewer HBM bytes). Every tile of one compute kind gives the same bits,
+                                  so the choice never changes C. */
 #define MGEMM_TILE_64x64 1   /* VALU: 4x4 micro-tile per thread (the pages' shape); MFMA: one 32x32
                                 tile per wave, K slice 64 where the grid gives each of 256 CUs one
                                 block at most, else 32 (chosen from the shape alone) */

@@ -146,14 +146,20 @@ def test_auto_fp32_tile(compute):
             for S in (1, 2, 3):
                 p = m.plan(M, N, K, stages=S, fill=fill, compute=compute)
                 want = (edge, edge)
-                # MFMA on the asynchronous ring of 2+ stages: 256x128 where
-                # 128x128 would be chosen (same rate, a third of the HBM bytes)
+                # MFMA on the asynchronous ring of 2 or 3 stages: 256x128 where
+                # 128x128 would be chosen and every CU gets an even number of
+                # 256x128 tiles (both shapes here: 2 and 8 per CU)
                 if compute == "mfma" and fill == "piped" and S >= 2 and edge == 128:
                     want = (256, 128)
                 assert (p["bm"], p["bn"]) == want, (compute, fill, M, N, K, S)
-    # the warp-specialised ring keeps 128x128
+    # the warp-specialised ring, deeper rings and odd or uneven 256x128 tile
+    # counts per CU keep 128x128 (N = K = 8192: 256x128 tiles per CU = M / 1024)
     p = m.plan(8192, 8192, 8192, stages=2, fill="piped_ws", compute="mfma")
     assert (p["bm"], p["bn"]) == (128, 128)
+    if compute == "mfma":
+        assert m.plan(8192, 8192, 8192, stages=4, compute="mfma")["bm"] == 128
+        for M, bm in ((6144, 256), (10240, 256), (5120, 128), (7168, 128), (8704, 128), (9728, 128)):
+            assert m.plan(M, 8192, 8192, stages=2, compute="mfma")["bm"] == bm, M
     # the ABI's plain entry point plans with the VALU tile and the same choice
     st, pl = m.mgemm_plan_sgemm(4099, 3001, 1537, A0, 1537, B0, 3001, C0, 3001, 2, 1, 0, 0, 0)
     assert st == m.OK and pl.bm == 64
